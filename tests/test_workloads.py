@@ -1,0 +1,140 @@
+"""The seeded workloads and the block pool: allocation, sharing, copy-on-write, placement."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import attention
+from workloads import CONFIGS, make_batch, make_layout
+from workloads.blocks import BlockPool, PoolExhausted, Sequence
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_blocks_are_taken_only_when_the_current_one_is_full():
+    g = _golden("block_manager_defaults.json")
+    for case in g["cases"]:
+        pool = BlockPool(400, g["block_size"])
+        seq = Sequence(pool)
+        seq.extend(case["tokens"])
+        assert len(seq.blocks) == case["blocks"]
+        assert pool.num_free == 400 - case["blocks"]
+
+
+def test_mean_last_block_waste_matches_the_pages():
+    g = _golden("block_size_waste.json")
+    rng = np.random.default_rng(0)
+    for case in g["cases"]:
+        P = case["block_size"]
+        lens = rng.integers(1, 4096, size=20000)
+        waste = [(-(-n // P)) * P - n for n in lens]
+        assert abs(np.mean(waste) - case["mean_last_block_waste_tokens"]) <= g["tolerance_tokens"]
+
+
+def test_fork_shares_and_write_copies_the_partial_block():
+    pool = BlockPool(16, 16)
+    parent = Sequence(pool)
+    parent.extend(20)                        # blocks: full + partial(4)
+    kids = [parent.fork() for _ in range(3)]
+    parent.free()
+    assert all(pool.refcount[b] == 3 for b in kids[0].blocks)
+    results = [k.append_slot() for k in kids]
+    copies = [c for _, c in results if c is not None]
+    assert len(copies) == 2                   # last holder writes in place
+    src = kids[2].blocks[-1]
+    assert all(c[0] == src for c in copies)
+    dsts = [c[1] for c in copies]
+    assert len(set(dsts)) == 2 and src not in dsts
+    assert pool.refcount[kids[0].blocks[0]] == 3   # the full block stays shared
+    # each kid's new slot is offset 4 of its own last block
+    for (slot, _), k in zip(results, kids):
+        assert slot == k.blocks[-1] * 16 + 4
+
+
+def test_fork_at_a_block_boundary_needs_no_copy():
+    pool = BlockPool(8, 16)
+    parent = Sequence(pool)
+    parent.extend(32)
+    kids = [parent.fork() for _ in range(2)]
+    parent.free()
+    assert all(k.append_slot()[1] is None for k in kids)
+
+
+def test_pool_exhaustion_is_a_clean_error_and_free_returns_blocks():
+    pool = BlockPool(2, 16)
+    seq = Sequence(pool)
+    seq.extend(32)
+    with pytest.raises(PoolExhausted):
+        seq.append_slot()
+    seq.free()
+    assert pool.num_free == 2
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_layout_invariants(name):
+    cfg = CONFIGS[name]
+    lay = make_layout(cfg)
+    P = cfg.block_size
+    S = cfg.num_seqs
+    assert lay.block_tables.shape == (S, cfg.max_blocks_per_seq)
+    assert (lay.context_lens >= 1).all() and (lay.context_lens <= cfg.max_context_len).all()
+    owner = {}
+    for s in range(S):
+        n = -(-int(lay.context_lens[s]) // P)
+        row = lay.block_tables[s]
+        assert (row[n:] == lay.poison_block).all()
+        assert lay.poison_block not in row[:n]
+        # the new token's slot is the last logical position of the sequence
+        assert attention.physical_slot(row, int(lay.context_lens[s]) - 1, P) == divmod(int(lay.slot_mapping[s]), P)
+        for j in range(n):
+            owner.setdefault(int(row[j]), set()).add(s)
+        # history slots hold data, the new token's slot is stale before the step
+        for t in range(int(lay.context_lens[s]) - 1):
+            b, o = attention.physical_slot(row, t, P)
+            if b not in set(lay.copy_pairs[:, 1].tolist()):
+                assert lay.history_valid[b, o]
+    assert not lay.history_valid[lay.poison_block].any()
+    # a block written this step (holding a new token) belongs to one sequence only
+    for s in range(S):
+        b = int(lay.slot_mapping[s]) // P
+        assert owner[b] == {s}
+    dst = lay.copy_pairs[:, 1]
+    assert len(set(dst.tolist())) == len(dst)
+    assert not set(dst.tolist()) & set(lay.copy_pairs[:, 0].tolist())
+    if cfg.ctx[0] != "beam":
+        assert len(lay.copy_pairs) == 0
+        assert all(len(v) == 1 for v in owner.values())
+
+
+def test_beam_layout_shares_prompt_blocks_four_ways():
+    cfg = CONFIGS["beam_cow"]
+    lay = make_layout(cfg)
+    assert len(lay.copy_pairs) > 0
+    for r in range(cfg.num_seqs // 4):
+        rows = lay.block_tables[4 * r:4 * r + 4, :256]
+        assert (rows == rows[0]).all()       # the 256 prompt blocks are shared by all 4 beams
+    assert make_layout(cfg).copy_pairs.tolist() == lay.copy_pairs.tolist()   # seeded
+
+
+def test_tiny_batch_values_and_poison():
+    b = make_batch(CONFIGS["tiny"])
+    assert b.q.shape == (4, 2, 64)
+    assert b.k_cache.shape == (64, 2, 16, 64)
+    valid = b.layout.history_valid
+    kc = b.k_cache.float().numpy()
+    assert np.isnan(kc.transpose(0, 2, 1, 3)[~valid]).all()
+    assert np.isfinite(kc.transpose(0, 2, 1, 3)[valid]).all()
+
+
+def test_fp8_pool_codes_are_never_nan_in_history():
+    import workloads.gen as gen
+    cfg = CONFIGS["beam_cow"]
+    codes = gen._fp8_codes((4096,), "cpu", 1).numpy()
+    assert not ((codes & 0x7F) == 0x7F).any()
+    assert ((codes >> 3) & 0xF).max() <= 14

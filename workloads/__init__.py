@@ -1,0 +1,7 @@
+"""Seeded synthetic decode workloads shared by the tests, the smoke check and the benchmark.
+
+Holds only random draws and block bookkeeping; none of the attention,
+quantisation or cache-write arithmetic lives here.
+"""
+from .configs import CONFIGS, WorkloadConfig  # noqa: F401
+from .gen import Batch, Layout, make_batch, make_layout  # noqa: F401
