@@ -1,0 +1,194 @@
+"""Benchmark of one paged decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config llama2_70b_gqa]
+
+A step is the whole hot path over one synthetic batch: copy-on-write block copies
+(when the batch has any), the cache write of every sequence's new token, then
+decode attention over the paged cache. Inputs are resident in HBM before timing.
+Consecutive steps rotate over --replicas independent batches (own pools and block
+tables), so each step reads KV bytes the previous steps did not touch: about 2 GB
+lie between two reads of the same batch, far beyond the 256 MB last-level cache.
+
+Prints one JSON line. `value` is KV-read GB/s of the whole step (algorithmic KV
+bytes / step time); `roofline` reports the decode kernel alone, timed with HIP
+events on the stream it runs on; `cpu_baseline` times the float64 CPU oracle on a
+bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
+DECODE_SOURCES = ("paged_kv_cache_409_amd/csrc/decode_mfma.hip", "paged_kv_cache_409_amd/csrc/decode_valu.hip",
+                  "paged_kv_cache_409_amd/csrc/decode_common.h", "paged_kv_cache_409_amd/csrc/pkv_device.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(config_name: str, kv_bytes: float):
+    """HBM traffic of one decode launch from committed counter runs, if they match this kernel."""
+    path = os.path.join(ROOT, "profiles", f"decode_traffic_{config_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama2_70b_gqa")
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=0, help="sequences the oracle times (0: auto)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: decode attention shards by kv head or sequence with no exchange, "
+              "and this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_cache_409_amd as pkv
+    from workloads import CONFIGS, make_batch
+    from workloads.gen import kv_bytes_logical, kv_bytes_unique
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    batches = [make_batch(cfg, dev, replica=r) for r in range(args.replicas)]
+    lay = batches[0].layout
+    kv_logical = kv_bytes_logical(cfg, lay.context_lens)
+    kv_unique = kv_bytes_unique(cfg, lay)
+    kv_alg = kv_unique                        # distinct bytes a step must read (= logical unless blocks are shared)
+    ws_bytes = pkv.workspace_size(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                                  cfg.max_context_len, cfg.partition_size)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(b.q) for b in batches]
+    n_pairs = len(lay.copy_pairs)
+
+    def step(i, ev=None):
+        b = batches[i % len(batches)]
+        if len(b.copy_pairs):
+            pkv.copy_blocks([b.k_cache], [b.v_cache], b.copy_pairs)
+        pkv.reshape_and_cache(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale, b.v_scale)
+        if ev is not None:
+            ev[0].record()
+        pkv.paged_attention_decode(outs[i % len(batches)], b.q, b.k_cache, b.v_cache, b.block_tables,
+                                   b.context_lens, b.scale, cfg.max_context_len, b.k_scale, b.v_scale,
+                                   cfg.partition_size, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    dec_avg_ms = float(dec_ms.mean())
+    achieved = kv_alg / (dec_avg_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "paged decode attention: achieved KV-read HBM GB/s (% of peak) and seqs/s",
+        "value": round(kv_alg / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"q {cfg.dtype}, kv {cfg.kv_dtype}; fp32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.description,
+            "num_seqs": cfg.num_seqs, "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": cfg.head_dim, "block_size": cfg.block_size, "max_context_len": cfg.max_context_len,
+            "partition_tokens": pkv.partition_tokens(cfg.num_seqs, cfg.num_kv_heads, cfg.max_context_len,
+                                                     cfg.partition_size),
+            "kv_bytes_algorithmic": kv_alg, "kv_bytes_logical": kv_logical, "copy_pairs": n_pairs,
+            "replicas": args.replicas, "parallelism": "single GPU",
+        },
+        "seqs_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
+        "decode_us": {"mean": round(dec_avg_ms * 1e3, 2), "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                      "p50": round(float(np.percentile(dec_ms, 50)) * 1e3, 2),
+                      "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(cfg.name, kv_alg),
+                     "kernel": "paged_decode_mfma" if cfg.group_size > 1 else "paged_decode_valu",
+                     "kernel_source_hash": kernel_source_hash()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, batches[0], args.cpu_sample_seqs)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(cfg, b, sample_seqs: int):
+    """Time the float64 oracle, single-threaded, on a bounded sample of the batch's sequences."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention
+
+    def bits(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.element_size() == 2 else t.view(torch.uint8).numpy()
+
+    # The pool already holds this step's copies and new tokens (the GPU wrote them during timing).
+    q, kc, vc = bits(b.q), bits(b.k_cache), bits(b.v_cache)
+    bt, ctx = b.block_tables.cpu().numpy(), b.context_lens.cpu().numpy()
+    run = lambda seqs: attention.paged_decode_attention(q, kc, vc, bt, ctx, cfg.scale, cfg.dtype, cfg.kv_dtype,
+                                                        b.k_scale, b.v_scale, seqs=seqs)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        run([0])
+        per_seq = max(time.perf_counter() - t0, 1e-4)
+        n = sample_seqs or int(min(cfg.num_seqs, max(1, 15.0 / per_seq)))
+        seqs = np.linspace(0, cfg.num_seqs - 1, n).round().astype(int).tolist()
+        t0 = time.perf_counter()
+        run(seqs)
+        dt = time.perf_counter() - t0
+    kv = int(ctx[seqs].astype(np.int64).sum()) * 2 * cfg.num_kv_heads * cfg.head_dim * (
+        1 if cfg.kv_dtype == "fp8_e4m3" else 2)
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "seqs_per_s": round(len(seqs) / dt, 2),
+            "cores": 1, "kind": "oracle",
+            "sample": f"{len(seqs)} of {cfg.num_seqs} sequences (all heads), float64 numpy, one thread, "
+                      f"{dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,186 @@
+/*
+ * pkv.h -- paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpkv.so. Three operations, all enqueued asynchronously on the caller's
+ * HIP stream:
+ *
+ *   pkv_paged_attention_decode  one decode step of attention over a paged KV cache
+ *   pkv_reshape_and_cache       write each new token's K/V row into its cache slot
+ *   pkv_copy_blocks             copy-on-write copies of whole KV blocks
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named *_cache, q, out, key, value, block_tables, context_lens,
+ *   slot_mapping, src_dst_pairs and workspace are DEVICE pointers; every other
+ *   pointer is a host pointer. All tensors are dense, row-major, in the shapes
+ *   given below, and 16-byte aligned.
+ * - The caller allocates and owns every buffer, including the workspace. The
+ *   library allocates no device memory and keeps no pointer after a call returns.
+ *   Buffers must stay alive until the stream has passed the enqueued work.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ * - Arguments are checked on the host before anything is enqueued; a violation
+ *   returns a negative pkv_status and enqueues nothing. No call aborts or throws.
+ *   PKV_ERR_HIP means the HIP runtime refused a launch.
+ * - Values inside device buffers (block ids, slots, context lengths) cannot be
+ *   checked on the host. The kernels never touch memory outside the buffers for any
+ *   such value: an out-of-range block id is read as zeros, an out-of-range slot or
+ *   copy pair is skipped, a context length is clamped to the block-table row.
+ *   The results of a sequence that hits one of these cases are unspecified.
+ * - Calls are reentrant; the library holds no global state.
+ *
+ * Cache layout (chosen for gfx950): k_cache and v_cache are separate tensors of
+ * shape [num_blocks, num_kv_heads, block_size, head_dim] with block_size = 16, so one
+ * kv head's slice of one block (16 token rows) is a single contiguous tile that a
+ * wavefront reads with 16-byte loads. A slot is the flat index block * 16 + offset.
+ *
+ * The method follows the pages on PagedAttention: the KV cache is cut into blocks
+ * of 16 token slots, placed anywhere in a shared pool and found through a
+ * per-sequence block table ("vLLM推理引擎PagedAttention原理与性能优化实战", §2.2;
+ * "vLLM 是什么…", §二); attention itself is the standard Softmax(Q K^T / sqrt(d)) V
+ * over the gathered K and V ("vLLM 推理优化技术深度调研报告", 维度一.1 误解二 and
+ * 维度一.3 公式 3-4).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_API_VERSION 1
+
+/* Element types. */
+typedef enum pkv_dtype {
+  PKV_F16 = 1,       /* IEEE binary16 */
+  PKV_BF16 = 2,      /* bfloat16 */
+  PKV_FP8_E4M3 = 3   /* OCP E4M3FN codes (cache only), read as code value * per-tensor fp32 scale */
+} pkv_dtype;
+
+/* Status codes: 0 on success, negative on error. */
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,         /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,        /* a size is out of range or sizes disagree */
+  PKV_ERR_DTYPE = -3,        /* unknown dtype, or a dtype combination that is not allowed */
+  PKV_ERR_UNSUPPORTED = -4,  /* valid request outside what the kernels implement (e.g. head_dim) */
+  PKV_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
+  PKV_ERR_ALIGN = -6,        /* a device pointer or stride breaks 16-byte alignment */
+  PKV_ERR_HIP = -7           /* the HIP runtime reported an error at launch */
+} pkv_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pkv_status_string(int status);
+
+/* PKV_API_VERSION of the library. */
+int pkv_api_version(void);
+
+/*
+ * Context-partition length, in tokens, that pkv_paged_attention_decode will use.
+ * partition_size > 0 is validated and returned as is (it must be a multiple of 16);
+ * 0 asks the library to choose: one partition per sequence when num_seqs *
+ * num_kv_heads work items already fill the GPU, otherwise the longest multiple of
+ * 256 tokens that gives about 2048 items. Returns a negative pkv_status on bad input.
+ */
+int pkv_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_context_len, int partition_size);
+
+/*
+ * Bytes of device workspace pkv_paged_attention_decode needs for these sizes (0 when
+ * every sequence fits one partition). The workspace holds fp32 partial results
+ * [num_seqs, num_q_heads, num_partitions, head_dim + 2]. Returns 0 on bad input.
+ */
+size_t pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                          int max_context_len, int partition_size);
+
+/*
+ * Decode-step attention over a paged KV cache.
+ *
+ * For every sequence s and query head h (kv head g = h / (num_q_heads / num_kv_heads)):
+ *   K_s[t] = k_cache[block_tables[s][t / 16], g, t % 16, :]  for t < context_lens[s]
+ *   (V_s likewise; an fp8 cache is read as code value * k_scale / v_scale)
+ *   out[s, h, :] = softmax(scale * K_s q[s, h]) V_s
+ * accumulated in fp32 and rounded (nearest even) to q's dtype. A sequence with
+ * context length 0 gets zeros. context_lens counts the newest token, so the caller
+ * runs pkv_reshape_and_cache for it first.
+ *
+ *   out            [num_seqs, num_q_heads, head_dim]          q_dtype (written)
+ *   q              [num_seqs, num_q_heads, head_dim]          q_dtype; sequence stride
+ *                  q_seq_stride elements (0 = num_q_heads * head_dim)
+ *   k_cache/v_cache[num_blocks, num_kv_heads, 16, head_dim]   kv_dtype
+ *   block_tables   [num_seqs, max_blocks_per_seq] int32       physical block ids
+ *   context_lens   [num_seqs] int32                            tokens to attend, <= max_context_len
+ *   q_dtype        PKV_F16 or PKV_BF16
+ *   kv_dtype       q_dtype, or PKV_FP8_E4M3
+ *   scale          logit scale (1/sqrt(head_dim) for standard attention)
+ *   k_scale/v_scale fp8 cache scales (ignored for 16-bit caches)
+ *   max_context_len upper bound of context_lens; sets the grid (host-side hint)
+ *   partition_size tokens per context partition, multiple of 16, or 0 (see
+ *                  pkv_decode_partition_tokens); more than one partition per
+ *                  sequence runs a second, merging kernel
+ *   workspace      device buffer of pkv_paged_attention_workspace_size() bytes
+ *                  (may be NULL when that size is 0)
+ *
+ * Supported: head_dim 64 or 128; num_q_heads a multiple of num_kv_heads with group
+ * size 1..16; block_size 16. Group size 1 runs on the vector ALUs, larger groups on
+ * the matrix cores.
+ */
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                               int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
+                               int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
+                               int64_t q_seq_stride, int partition_size,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Write the K and V rows of num_tokens new tokens into their cache slots
+ * ("vLLM 是什么…", §二: a token goes into the current block, a new block is taken only
+ * when that one is full; the slot numbers come from the caller's block manager).
+ *
+ *   key/value      [num_tokens, num_kv_heads, head_dim] in_dtype; token strides
+ *                  key_stride / value_stride elements (0 = num_kv_heads * head_dim)
+ *   slot_mapping   [num_tokens] int64; slot = block * 16 + offset; a negative slot is skipped
+ *   k_cache/v_cache[num_blocks, num_kv_heads, 16, head_dim] kv_dtype (one layer)
+ *   in_dtype       PKV_F16 or PKV_BF16
+ *   kv_dtype       in_dtype (the row is copied bit for bit) or PKV_FP8_E4M3, where every
+ *                  element is stored as E4M3FN(fl32(x / scale)): IEEE fp32 division,
+ *                  round to nearest even, saturating to +-448, NaN kept
+ *                  ("vLLM推理引擎PagedAttention原理与性能优化实战", §5.2 names FP8 caches;
+ *                  the format and rounding are this library's reading)
+ *   k_scale/v_scale fp8 scales, finite and > 0 (ignored for 16-bit caches)
+ *
+ * Two tokens mapped to one slot in one call is a caller error (the winner is unspecified).
+ */
+int pkv_reshape_and_cache(const void* key, const void* value, const int64_t* slot_mapping,
+                          void* k_cache, void* v_cache,
+                          int num_tokens, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                          int in_dtype, int kv_dtype, float k_scale, float v_scale,
+                          int64_t key_stride, int64_t value_stride, void* stream);
+
+/*
+ * Copy-on-write block copies ("vLLM推理引擎PagedAttention原理与性能优化实战", §3.2:
+ * a block shared by several sequences is read-only; the first write into it takes a
+ * fresh block and copies the old contents there). For every pair (src, dst) and every
+ * layer l: k_caches[l][dst] = k_caches[l][src] and v_caches[l][dst] = v_caches[l][src],
+ * whole blocks, byte for byte.
+ *
+ *   k_caches/v_caches host arrays of num_layers device pointers, each a cache of
+ *                  num_blocks blocks of block_bytes bytes
+ *   src_dst_pairs  device [num_pairs, 2] int64
+ *   block_bytes    bytes of one block of one layer's K (= V) cache:
+ *                  num_kv_heads * 16 * head_dim * element size; a multiple of 16
+ *
+ * Every dst must be distinct and must not be a src in the same call (a copy goes to a
+ * freshly taken block); num_pairs = 0 is a no-op.
+ */
+int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers,
+                    const int64_t* src_dst_pairs, int num_pairs, int64_t block_bytes, int64_t num_blocks,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

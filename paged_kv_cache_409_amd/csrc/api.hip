@@ -1,0 +1,239 @@
+// C ABI of libpkv.so: host-side validation and dispatch. Contract in include/pkv.h.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/pkv.h"
+#include "pkv_launch.h"
+
+
+namespace {
+
+constexpr int kMaxGroup = 16;
+constexpr int kMaxPartTokens = 32768;     // block-table slice of one partition: 2048 ids in LDS
+constexpr int kTargetItems = 2048;        // about two resident wavefronts per SIMD
+constexpr size_t kAlign = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool is16bit(int t) { return t == PKV_F16 || t == PKV_BF16; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  int part_tokens;
+  int num_parts;
+  size_t ml_bytes;
+  size_t ws_bytes;
+};
+
+int resolve_partition(int num_seqs, int num_kv_heads, int max_context_len, int partition_size) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return PKV_ERR_SHAPE;
+  if (partition_size < 0 || partition_size % 16 != 0 || partition_size > kMaxPartTokens) return PKV_ERR_SHAPE;
+  if (partition_size > 0) return partition_size;
+  const int whole = (int)round_up((size_t)(max_context_len > 0 ? max_context_len : 1), 16);
+  const long long units = (long long)num_seqs * num_kv_heads;
+  int part = whole;
+  if (units > 0 && units < kTargetItems) {
+    const long long want = (kTargetItems + units - 1) / units;
+    part = (int)round_up((size_t)((max_context_len + want - 1) / want), 256);
+    if (part > whole) part = whole;
+  }
+  return part > kMaxPartTokens ? kMaxPartTokens : part;
+}
+
+int make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_context_len,
+              int partition_size, Plan* plan) {
+  const int part = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+  if (part < 0) return part;
+  plan->part_tokens = part;
+  plan->num_parts = (max_context_len + part - 1) / part;
+  if (plan->num_parts < 1) plan->num_parts = 1;
+  plan->ml_bytes = 0;
+  plan->ws_bytes = 0;
+  if (plan->num_parts > 1) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * plan->num_parts;
+    plan->ml_bytes = round_up(rows * 2 * sizeof(float), kAlign);
+    plan->ws_bytes = plan->ml_bytes + round_up(rows * (size_t)head_dim * sizeof(float), kAlign);
+  }
+  return PKV_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "a size is out of range or sizes disagree";
+    case PKV_ERR_DTYPE: return "unknown or disallowed dtype combination";
+    case PKV_ERR_UNSUPPORTED: return "request outside what the kernels implement";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_ALIGN: return "a device pointer or stride is not 16-byte aligned";
+    case PKV_ERR_HIP: return "the HIP runtime reported an error";
+    default: return "unknown status";
+  }
+}
+
+int pkv_api_version(void) { return PKV_API_VERSION; }
+
+int pkv_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_context_len, int partition_size) {
+  return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+}
+
+size_t pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                          int max_context_len, int partition_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  Plan plan;
+  if (make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size, &plan) != PKV_OK)
+    return 0;
+  return plan.ws_bytes;
+}
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                               int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
+                               int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
+                               int64_t q_seq_stride, int partition_size,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      max_context_len < 0)
+    return PKV_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * 16) return PKV_ERR_SHAPE;
+  if (!is16bit(q_dtype)) return PKV_ERR_DTYPE;
+  if (kv_dtype != q_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (block_size != 16 || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  if (group > kMaxGroup) return PKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  if (kv_dtype == PKV_FP8_E4M3 &&
+      !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return PKV_ERR_SHAPE;
+  if (q_seq_stride == 0) q_seq_stride = (int64_t)num_q_heads * head_dim;
+  if (q_seq_stride < (int64_t)num_q_heads * head_dim) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || q_seq_stride % 8 != 0)
+    return PKV_ERR_ALIGN;
+
+  Plan plan;
+  const int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size, &plan);
+  if (st != PKV_OK) return st;
+  const long long items = (long long)num_seqs * num_kv_heads * plan.num_parts;
+  if (items > (1LL << 30)) return PKV_ERR_SHAPE;
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  }
+
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.part_ml = plan.ws_bytes ? reinterpret_cast<float*>(workspace) : nullptr;
+  a.part_o = plan.ws_bytes ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + plan.ml_bytes)
+                           : nullptr;
+  a.q_seq_stride = q_seq_stride;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_parts = plan.num_parts;
+  a.part_blocks = plan.part_tokens / 16;
+  a.num_items = (int)items;
+  const float log2e = 1.4426950408889634f;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+  a.qk_scale_log2 = scale * log2e * (fp8 ? k_scale : 1.0f);
+  a.v_scale = fp8 ? v_scale : 1.0f;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int qt = q_dtype == PKV_BF16 ? pkv::kBF16 : pkv::kF16;
+  const int kt = fp8 ? pkv::kFP8 : qt;
+  hipError_t e = group == 1 ? pkv::launch_decode_valu(a, qt, kt, head_dim, s)
+                            : pkv::launch_decode_mfma(a, qt, kt, head_dim, s);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  if (plan.num_parts > 1) {
+    pkv::ReduceArgs r;
+    r.out = out;
+    r.part_ml = a.part_ml;
+    r.part_o = a.part_o;
+    r.context_lens = context_lens;
+    r.num_seqs = num_seqs;
+    r.num_q_heads = num_q_heads;
+    r.num_parts = plan.num_parts;
+    r.part_tokens = plan.part_tokens;
+    r.max_tokens = max_blocks_per_seq * 16;
+    r.v_scale = a.v_scale;
+    e = pkv::launch_decode_reduce(r, qt, head_dim, s);
+  }
+  return hip_status(e);
+}
+
+int pkv_reshape_and_cache(const void* key, const void* value, const int64_t* slot_mapping,
+                          void* k_cache, void* v_cache,
+                          int num_tokens, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                          int in_dtype, int kv_dtype, float k_scale, float v_scale,
+                          int64_t key_stride, int64_t value_stride, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (!is16bit(in_dtype)) return PKV_ERR_DTYPE;
+  if (kv_dtype != in_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (block_size != 16 || head_dim <= 0 || head_dim % 8 != 0 || head_dim > 1024) return PKV_ERR_UNSUPPORTED;
+  if (kv_dtype == PKV_FP8_E4M3 &&
+      !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return PKV_ERR_SHAPE;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (key_stride == 0) key_stride = row;
+  if (value_stride == 0) value_stride = row;
+  if (key_stride < row || value_stride < row) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) || key_stride % 8 != 0 ||
+      value_stride % 8 != 0)
+    return PKV_ERR_ALIGN;
+  if ((int64_t)num_tokens * num_kv_heads * (head_dim / 8) > (1LL << 40)) return PKV_ERR_SHAPE;
+
+  pkv::CacheWriteArgs a;
+  a.key = key;
+  a.value = value;
+  a.slot_mapping = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.key_stride = key_stride;
+  a.value_stride = value_stride;
+  a.num_slots = num_blocks * 16;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  const int it = in_dtype == PKV_BF16 ? pkv::kBF16 : pkv::kF16;
+  const int kt = kv_dtype == PKV_FP8_E4M3 ? pkv::kFP8 : it;
+  return hip_status(pkv::launch_reshape_and_cache(a, it, kt, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers,
+                    const int64_t* src_dst_pairs, int num_pairs, int64_t block_bytes, int64_t num_blocks,
+                    void* stream) {
+  if (num_layers < 0 || num_pairs < 0 || num_blocks <= 0 || block_bytes <= 0 || block_bytes % 16 != 0)
+    return PKV_ERR_SHAPE;
+  if (num_layers == 0 || num_pairs == 0) return PKV_OK;
+  if (!k_caches || !v_caches || !src_dst_pairs) return PKV_ERR_NULL;
+  for (int l = 0; l < num_layers; ++l) {
+    if (!k_caches[l] || !v_caches[l]) return PKV_ERR_NULL;
+    if (!aligned16(k_caches[l]) || !aligned16(v_caches[l])) return PKV_ERR_ALIGN;
+  }
+  const long long chunk_wgs = (block_bytes / 16 + 255) / 256;
+  if ((long long)num_pairs * chunk_wgs > (1LL << 31) - 1) return PKV_ERR_SHAPE;
+  return hip_status(pkv::launch_copy_blocks(k_caches, v_caches, num_layers, src_dst_pairs, num_pairs, block_bytes,
+                                            num_blocks, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

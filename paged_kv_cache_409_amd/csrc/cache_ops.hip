@@ -1,0 +1,135 @@
+// Writing new tokens into their cache slots, and copy-on-write block copies.
+//
+// * A decoded token's K and V rows go into the slot the block manager assigned it
+//   (a fresh block is taken only when the current one is full: "vLLM 是什么…", §二).
+//   The slot is the flat index block * 16 + offset; a negative slot is skipped.
+//   For an fp8 cache each value is quantised on the way in:
+//   code = E4M3FN(fl32(x / scale)), round to nearest even, saturating at +-448, NaN
+//   kept (the pages only say FP8 halves KV memory, "vLLM推理引擎PagedAttention原理与
+//   性能优化实战", §5.2; the format and rounding are this library's reading).
+// * Sequences sharing a block see it read-only; the first write into it copies the
+//   whole block to a fresh one (same page, §3.2). copy_blocks performs those copies
+//   for K and V of every layer given.
+#include "pkv_launch.h"
+
+namespace pkv {
+
+// OCP E4M3FN encoder, written from the format's definition: bias 7, 3 mantissa bits,
+// no infinities, S.1111.111 = NaN, largest finite 448, smallest subnormal 2^-9.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const float ax = fabsf(x);
+  if (ax != ax) return 0x7Fu | sign;                 // NaN
+  if (ax >= 448.0f) return 0x7Eu | sign;             // saturate (infinities too)
+  if (ax < 0.015625f) {                              // below 2^-6: multiples of 2^-9
+    return (uint32_t)__builtin_rintf(ax * 512.0f) | sign;   // exact scaling, then RNE
+  }
+  const uint32_t ab = __float_as_uint(ax);
+  const uint32_t r = ab + 0x7FFFFu + ((ab >> 20) & 1u);     // RNE at the 3rd mantissa bit
+  const uint32_t e = (r >> 23) - 127u + 7u;                   // biased E4M3 exponent, 1..15
+  return sign | (e << 3) | ((r >> 20) & 7u);
+}
+
+
+// One thread per 8 consecutive elements of one (token, kv head) row.
+template <int IT, int KVT>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a) {
+  const int chunks = a.head_dim / 8;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= (int64_t)a.num_tokens * a.num_kv_heads * chunks) return;
+  const int c = (int)(tid % chunks);
+  const int h = (int)((tid / chunks) % a.num_kv_heads);
+  const int64_t t = tid / ((int64_t)chunks * a.num_kv_heads);
+  const int64_t slot = a.slot_mapping[t];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t blk = slot / kBlock, off = slot % kBlock;
+  const int64_t dst = ((blk * a.num_kv_heads + h) * kBlock + off) * a.head_dim + 8 * c;
+  const u32x4 kin = *(const u32x4*)((const uint16_t*)a.key + t * a.key_stride + (int64_t)h * a.head_dim + 8 * c);
+  const u32x4 vin = *(const u32x4*)((const uint16_t*)a.value + t * a.value_stride + (int64_t)h * a.head_dim + 8 * c);
+  if constexpr (KVT == kFP8) {
+    u32x2 ko, vo;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t kk = 0, vv = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kp = kin[2 * w + e / 2], vp = vin[2 * w + e / 2];
+        const float kx = (e & 1) ? hi16<IT>(kp) : lo16<IT>(kp);
+        const float vx = (e & 1) ? hi16<IT>(vp) : lo16<IT>(vp);
+        kk |= e4m3_from_f32(kx / a.k_scale) << (8 * e);
+        vv |= e4m3_from_f32(vx / a.v_scale) << (8 * e);
+      }
+      ko[w] = kk;
+      vo[w] = vv;
+    }
+    *(u32x2*)((uint8_t*)a.k_cache + dst) = ko;
+    *(u32x2*)((uint8_t*)a.v_cache + dst) = vo;
+  } else {
+    *(u32x4*)((uint16_t*)a.k_cache + dst) = kin;
+    *(u32x4*)((uint16_t*)a.v_cache + dst) = vin;
+  }
+}
+
+hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, int in_type, int kv_type, hipStream_t stream) {
+  const int64_t threads = (int64_t)a.num_tokens * a.num_kv_heads * (a.head_dim / 8);
+  if (threads == 0) return hipSuccess;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+#define PKV_CASE(IT, KVT)                                                                      \
+  if (in_type == IT && kv_type == KVT) {                                                        \
+    hipLaunchKernelGGL((reshape_and_cache_kernel<IT, KVT>), grid, dim3(256), 0, stream, a);     \
+    return hipGetLastError();                                                                   \
+  }
+  PKV_CASE(kBF16, kBF16) PKV_CASE(kF16, kF16) PKV_CASE(kBF16, kFP8) PKV_CASE(kF16, kFP8)
+#undef PKV_CASE
+  return hipErrorInvalidValue;
+}
+
+constexpr int kMaxCopyLayers = 64;
+
+struct CopyArgs {
+  void* k[kMaxCopyLayers];
+  void* v[kMaxCopyLayers];
+  const int64_t* pairs;       // [num_pairs, 2] (src, dst)
+  int64_t block_bytes;        // bytes of one block of one layer's K (or V) cache
+  int64_t num_blocks;
+  int num_pairs;
+  int chunk_wgs;              // workgroups per (pair, layer, tensor)
+};
+
+// blockIdx.x = pair * chunk_wgs + chunk group, blockIdx.y = layer, blockIdx.z = 0 (K) / 1 (V).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
+  const int pair = blockIdx.x / a.chunk_wgs;
+  const int64_t chunk = (int64_t)(blockIdx.x % a.chunk_wgs) * 256 + threadIdx.x;
+  if (chunk * 16 >= a.block_bytes) return;
+  const int64_t src = a.pairs[2 * pair], dst = a.pairs[2 * pair + 1];
+  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+  uint8_t* base = (uint8_t*)(blockIdx.z == 0 ? a.k[blockIdx.y] : a.v[blockIdx.y]);
+  const u32x4 x = *(const u32x4*)(base + src * a.block_bytes + chunk * 16);
+  *(u32x4*)(base + dst * a.block_bytes + chunk * 16) = x;
+}
+
+hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers,
+                              const int64_t* pairs, int num_pairs, int64_t block_bytes, int64_t num_blocks,
+                              hipStream_t stream) {
+  if (num_pairs == 0 || num_layers == 0) return hipSuccess;
+  CopyArgs a;
+  a.pairs = pairs;
+  a.block_bytes = block_bytes;
+  a.num_blocks = num_blocks;
+  a.num_pairs = num_pairs;
+  a.chunk_wgs = (int)((block_bytes / 16 + 255) / 256);
+  for (int l0 = 0; l0 < num_layers; l0 += kMaxCopyLayers) {
+    const int nl = num_layers - l0 < kMaxCopyLayers ? num_layers - l0 : kMaxCopyLayers;
+    for (int l = 0; l < nl; ++l) {
+      a.k[l] = k_caches[l0 + l];
+      a.v[l] = v_caches[l0 + l];
+    }
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs * a.chunk_wgs, nl, 2), dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace pkv

@@ -1,0 +1,61 @@
+// Parameters and helpers shared by the paged decode-attention kernels.
+#pragma once
+
+#include "pkv_device.h"
+
+namespace pkv {
+
+// One launch of the decode main kernel. Work item = (sequence, kv head, context
+// partition); one wavefront per item.
+struct DecodeArgs {
+  void* out;                      // [S, Hq, D] q dtype (written when num_parts == 1)
+  const void* q;                  // [S, Hq, D] q dtype, sequence stride q_seq_stride elements
+  const void* k_cache;            // [NB, Hkv, 16, D]
+  const void* v_cache;            // [NB, Hkv, 16, D]
+  const int32_t* block_tables;    // [S, max_blocks]
+  const int32_t* context_lens;    // [S]
+  float* part_ml;                 // [S, Hq, num_parts, 2]: running max (log2 units), sum
+  float* part_o;                  // [S, Hq, num_parts, D]: unnormalised weighted sums
+  int64_t q_seq_stride;
+  int64_t num_blocks;
+  int num_seqs, num_q_heads, num_kv_heads, group;
+  int max_blocks;                 // block-table row length
+  int num_parts;                  // partitions per sequence (grid dimension)
+  int part_blocks;                // KV blocks per partition
+  int num_items;                  // num_seqs * num_kv_heads * num_parts
+  float qk_scale_log2;            // scale * log2(e) (* k_scale for an fp8 cache)
+  float v_scale;                  // 1, or v_scale for an fp8 cache
+};
+
+// Workgroup -> work item. Workgroups are dealt to the 8 XCDs round-robin; this map
+// gives each run of 4 consecutive items (the 4 beams of one request when sequences
+// are laid out request-major) to a single XCD, so blocks they share stay in that
+// XCD's L2. The grid is padded to a multiple of 32; ids past num_items do nothing.
+__device__ __forceinline__ int item_of_workgroup(int w) {
+  const int xcd = w & 7, k = w >> 3;
+  return (((k >> 2) << 3) + xcd) * 4 + (k & 3);
+}
+
+struct Item {
+  int s, g, p;
+};
+
+// Items are ordered (kv head, partition, sequence) with the sequence fastest.
+__device__ __forceinline__ Item decode_item(int j, const DecodeArgs& a) {
+  Item it;
+  it.s = j % a.num_seqs;
+  const int r = j / a.num_seqs;
+  it.p = r % a.num_parts;
+  it.g = r / a.num_parts;
+  return it;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+}  // namespace pkv

@@ -1,0 +1,131 @@
+"""Python binding of libpkv.so over torch tensors: argument marshalling only.
+
+Every step of the hot path runs in the HIP kernels behind the C ABI; this module
+reads shapes, dtypes and device pointers off torch tensors and raises PkvError on a
+non-zero status. torch supplies device memory and the current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import PKV_BF16, PKV_F16, PKV_FP8_E4M3
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.load().pkv_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+_DT = {torch.float16: PKV_F16, torch.bfloat16: PKV_BF16, torch.uint8: PKV_FP8_E4M3,
+       torch.float8_e4m3fn: PKV_FP8_E4M3}
+
+
+def _dtype(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("pkv kernels need device tensors")
+        if not t.is_contiguous():
+            raise ValueError("pkv kernels need contiguous tensors")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PkvError(fn, status)
+
+
+def partition_tokens(num_seqs: int, num_kv_heads: int, max_context_len: int, partition_size: int = 0) -> int:
+    r = _lib.load().pkv_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_size)
+    if r < 0:
+        raise PkvError("pkv_decode_partition_tokens", r)
+    return r
+
+
+def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,
+                   partition_size: int = 0) -> int:
+    return _lib.load().pkv_paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                          max_context_len, partition_size)
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                           max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0,
+                           partition_size: int = 0, workspace: torch.Tensor | None = None, stream=None):
+    """out[s, h] = softmax(scale * K_s q[s, h]) V_s over the paged cache (see pkv_paged_attention_decode)."""
+    _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+    S, Hq, D = q.shape
+    NB, Hkv, P, D2 = k_cache.shape
+    if tuple(out.shape) != (S, Hq, D) or tuple(v_cache.shape) != tuple(k_cache.shape) or D2 != D:
+        raise ValueError("shape mismatch")
+    if out.dtype != q.dtype or v_cache.dtype != k_cache.dtype:
+        raise ValueError("dtype mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables / context_lens shape mismatch")
+    need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.load().pkv_paged_attention_decode(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), S, Hq, Hkv, D, P, NB, block_tables.shape[1], max_context_len,
+        _dtype(q), _dtype(k_cache), scale, k_scale, v_scale, 0, partition_size, ws_ptr, ws_bytes,
+        _stream(stream))
+    _check("pkv_paged_attention_decode", st)
+    return out
+
+
+def reshape_and_cache(key, value, slot_mapping, k_cache, v_cache, k_scale: float = 1.0, v_scale: float = 1.0,
+                      stream=None) -> None:
+    """Write key/value [T, Hkv, D] rows into their slots of one layer's caches."""
+    _dev(key, value, slot_mapping, k_cache, v_cache)
+    T, Hkv, D = key.shape
+    NB, Hkv2, P, D2 = k_cache.shape
+    if tuple(value.shape) != (T, Hkv, D) or Hkv2 != Hkv or D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    if value.dtype != key.dtype or v_cache.dtype != k_cache.dtype:
+        raise ValueError("dtype mismatch")
+    st = _lib.load().pkv_reshape_and_cache(
+        key.data_ptr(), value.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        T, Hkv, D, P, NB, _dtype(key), _dtype(k_cache), k_scale, v_scale, 0, 0, _stream(stream))
+    _check("pkv_reshape_and_cache", st)
+
+
+def copy_blocks(k_caches, v_caches, src_dst_pairs, stream=None) -> None:
+    """For each (src, dst) pair and layer: cache[dst] = cache[src], K and V."""
+    if len(k_caches) != len(v_caches):
+        raise ValueError("k_caches and v_caches differ in length")
+    _dev(src_dst_pairs, *k_caches, *v_caches)
+    if src_dst_pairs.dtype != torch.int64 or src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be int64 [num_pairs, 2]")
+    ref = k_caches[0]
+    for c in (*k_caches, *v_caches):
+        if c.shape != ref.shape or c.dtype != ref.dtype:
+            raise ValueError("all caches must share shape and dtype")
+    n = len(k_caches)
+    kp = (ctypes.c_void_p * n)(*[c.data_ptr() for c in k_caches])
+    vp = (ctypes.c_void_p * n)(*[c.data_ptr() for c in v_caches])
+    block_bytes = ref[0].numel() * ref.element_size()
+    st = _lib.load().pkv_copy_blocks(kp, vp, n, src_dst_pairs.data_ptr(), src_dst_pairs.shape[0], block_bytes,
+                                     ref.shape[0], _stream(stream))
+    _check("pkv_copy_blocks", st)

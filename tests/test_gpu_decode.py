@@ -1,0 +1,156 @@
+"""Parity of the HIP decode path with the oracle (element by element), plus the
+method's invariants on the GPU: placement invariance, shared = copied blocks,
+determinism, split = unsplit, stale slots never read."""
+import numpy as np
+import pytest
+import torch
+
+from tests._gpu import (HostBatch, device_batch, gpu_decode, gpu_step, max_err, oracle_caches_after_step,
+                        oracle_decode, say, tol)
+from workloads import WorkloadConfig
+
+pytestmark = pytest.mark.gpu
+
+
+def small_cfg(G, D, dtype, kv_dtype, S=10, Hkv=2, ctx=("uniform", 1, 600), max_ctx=600, seed=7, nb=None):
+    return WorkloadConfig(
+        name=f"small_G{G}_D{D}_{dtype}_{kv_dtype}", num_seqs=S, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+        head_dim=D, num_blocks=nb or S * (max_ctx // 16 + 3) + 8, seed=seed, dtype=dtype, kv_dtype=kv_dtype,
+        ctx=ctx, max_context_len=max_ctx, kv_scale=(1 / 128 if kv_dtype == "fp8_e4m3" else 1.0))
+
+
+DTYPES = [("f16", "f16"), ("bf16", "bf16"), ("bf16", "fp8_e4m3"), ("f16", "fp8_e4m3")]
+
+
+def _step_case(cfg, partition_size=0):
+    b = device_batch(cfg)
+    h = HostBatch(b)
+    say(cfg.name, "partition", partition_size)
+    out = gpu_step(b, partition_size)
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches_after_step(h)
+    ref = oracle_decode(h, kc, vc)
+    err = max_err(out, ref)
+    assert err <= tol(cfg), f"{cfg.name}: max abs error {err}"
+    return b, out
+
+
+@pytest.mark.parametrize("dtype,kv_dtype", DTYPES)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_decode_step_matches_oracle(G, D, dtype, kv_dtype):
+    _step_case(small_cfg(G, D, dtype, kv_dtype))
+
+
+@pytest.mark.parametrize("partition", [16, 48, 256, 512])
+@pytest.mark.parametrize("G,dtype,kv_dtype", [(1, "f16", "f16"), (8, "bf16", "bf16"), (4, "bf16", "fp8_e4m3")])
+def test_split_context_matches_oracle_and_unsplit(G, dtype, kv_dtype, partition):
+    cfg = small_cfg(G, 128, dtype, kv_dtype, S=6, ctx=("uniform", 1, 1100), max_ctx=1100)
+    b, split = _step_case(cfg, partition)
+    whole = gpu_decode(b, partition_size=0)
+    torch.cuda.synchronize()
+    diff = (split.float() - whole.float()).abs().max().item()
+    assert diff <= 2 * tol(cfg)
+
+
+@pytest.mark.parametrize("G,dtype,kv_dtype", [(1, "f16", "f16"), (8, "bf16", "bf16"), (4, "bf16", "fp8_e4m3")])
+def test_context_lengths_at_block_and_table_edges(G, dtype, kv_dtype):
+    # 1, 15, 16, 17, 31, 32, 33 tokens and a completely full block-table row (5 blocks).
+    ctx = [1, 15, 16, 17, 31, 32, 33, 80]
+    cfg = small_cfg(G, 128, dtype, kv_dtype, S=len(ctx), ctx=("fixed", ctx), max_ctx=80)
+    _step_case(cfg)
+    _step_case(cfg, partition_size=16)
+
+
+@pytest.mark.parametrize("G", [1, 8])
+def test_zero_length_context_gives_zeros(G):
+    cfg = small_cfg(G, 128, "bf16", "bf16", S=6, ctx=("uniform", 1, 200), max_ctx=200)
+    b = device_batch(cfg)
+    h = HostBatch(b)
+    say(cfg.name, "zero-length rows")
+    gpu_step(b)
+    kc, vc = oracle_caches_after_step(h)
+    ctx = b.context_lens.clone()
+    ctx[1] = 0
+    ctx[4] = 0
+    for part in (0, 64):
+        out = gpu_decode(b, partition_size=part, context_lens=ctx)
+        torch.cuda.synchronize()
+        assert (out[1] == 0).all() and (out[4] == 0).all()
+        ref = oracle_decode(h, kc, vc, context_lens=ctx.cpu().numpy())
+        assert max_err(out, ref) <= tol(cfg)
+
+
+@pytest.mark.parametrize("G,dtype,kv_dtype", [(1, "f16", "f16"), (8, "bf16", "bf16"), (4, "bf16", "fp8_e4m3")])
+def test_output_is_bit_identical_under_block_permutation(G, dtype, kv_dtype):
+    cfg = small_cfg(G, 128, dtype, kv_dtype, S=8, ctx=("uniform", 1, 400), max_ctx=400)
+    b = device_batch(cfg)
+    say(cfg.name, "placement")
+    a_out = gpu_step(b)
+    perm = torch.randperm(cfg.num_blocks, generator=torch.Generator().manual_seed(3)).cuda()
+    kc = torch.empty_like(b.k_cache)
+    vc = torch.empty_like(b.v_cache)
+    kc[perm] = b.k_cache
+    vc[perm] = b.v_cache
+    b.block_tables = perm.to(torch.int32)[b.block_tables.long()].contiguous()
+    b_out = gpu_decode(b, k_cache=kc, v_cache=vc)
+    again = gpu_decode(b, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    assert torch.equal(a_out.view(torch.int16), b_out.view(torch.int16))
+    assert torch.equal(b_out.view(torch.int16), again.view(torch.int16))   # deterministic
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_shared_prefix_blocks_equal_private_copies(kv_dtype):
+    # Beams reading shared prefix blocks give bit-identical outputs to beams reading
+    # private copies of every block.
+    cfg = WorkloadConfig(name="beam_small", num_seqs=8, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                         num_blocks=1024, seed=11, dtype="bf16", kv_dtype=kv_dtype, ctx=("beam", 64, 0, 40, 4),
+                         max_context_len=64 + 40 + 1, kv_scale=(1 / 128 if kv_dtype == "fp8_e4m3" else 1.0))
+    b = device_batch(cfg)
+    h = HostBatch(b)
+    assert len(h.copy_pairs) > 0
+    say(cfg.name, kv_dtype, "shared vs private")
+    shared = gpu_step(b)
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches_after_step(h)
+    assert max_err(shared, oracle_decode(h, kc, vc)) <= tol(cfg)
+    # private copies: give every (sequence, logical block) its own fresh physical block
+    bt = b.block_tables.cpu().numpy()
+    nb = -(-b.context_lens.cpu().numpy() // 16)
+    used = set(int(x) for s in range(cfg.num_seqs) for x in bt[s, :nb[s]])
+    used.add(b.layout.poison_block)
+    free = [x for x in range(cfg.num_blocks) if x not in used]
+    new_bt = bt.copy()
+    src, dst = [], []
+    for s in range(cfg.num_seqs):
+        for j in range(nb[s]):
+            f = free.pop()
+            src.append(int(bt[s, j]))
+            dst.append(f)
+            new_bt[s, j] = f
+    idx_s = torch.tensor(src, device="cuda")
+    idx_d = torch.tensor(dst, device="cuda")
+    b.k_cache[idx_d] = b.k_cache[idx_s]
+    b.v_cache[idx_d] = b.v_cache[idx_s]
+    b.block_tables = torch.from_numpy(new_bt).cuda()
+    private = gpu_decode(b)
+    torch.cuda.synchronize()
+    assert torch.equal(shared.view(torch.int16), private.view(torch.int16))
+
+
+def test_fp8_cache_over_every_finite_code():
+    cfg = small_cfg(4, 128, "bf16", "fp8_e4m3", S=6, ctx=("uniform", 20, 300), max_ctx=300)
+    b = device_batch(cfg)
+    g = torch.Generator().manual_seed(5)
+    valid = torch.from_numpy(b.layout.history_valid)[:, None, :, None].expand(b.k_cache.shape).cuda()
+    for cache in (b.k_cache, b.v_cache):
+        codes = torch.randint(0, 254, cache.shape, generator=g, dtype=torch.int32)
+        codes = torch.where(codes >= 0x7F, codes + 1, codes).to(torch.uint8).cuda()   # skip 0x7F, 0xFF
+        cache.copy_(torch.where(valid, codes, cache))
+    h = HostBatch(b)
+    say(cfg.name, "all fp8 codes")
+    out = gpu_step(b)
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches_after_step(h)
+    assert max_err(out, oracle_decode(h, kc, vc)) <= tol(cfg)

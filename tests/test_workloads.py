@@ -4,6 +4,7 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 from oracle import attention
 from workloads import CONFIGS, make_batch, make_layout
@@ -132,9 +133,12 @@ def test_tiny_batch_values_and_poison():
     assert np.isfinite(kc.transpose(0, 2, 1, 3)[valid]).all()
 
 
-def test_fp8_pool_codes_are_never_nan_in_history():
+def test_fp8_pool_codes_are_never_nan(monkeypatch):
     import workloads.gen as gen
-    cfg = CONFIGS["beam_cow"]
-    codes = gen._fp8_codes((4096,), "cpu", 1).numpy()
+    codes = gen._fp8_codes((1 << 20,), "cpu", 1).numpy()
     assert not ((codes & 0x7F) == 0x7F).any()
     assert ((codes >> 3) & 0xF).max() <= 14
+    # a geometric draw of 0 (uniform draw exactly 1) must not produce the NaN code
+    monkeypatch.setattr(torch.Tensor, "geometric_", lambda self, p, generator=None: self.fill_(0.0))
+    zero = gen._fp8_codes((4096,), "cpu", 2).numpy()
+    assert ((zero >> 3) & 0xF).max() == 14

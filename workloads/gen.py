@@ -20,7 +20,7 @@ torch generator per tensor for the values):
   the new token then copies every still-shared partial last block (copy-on-write).
 * values: q, the new token's K/V, and the pool's history slots are N(0, 1) drawn
   in fp32 and rounded to the stored 16-bit type. An fp8 pool is drawn as codes:
-  random sign, exponent field 15 - G with G ~ Geometric(1/2) (floored at 0),
+  random sign, exponent field 15 - G with G ~ Geometric(1/2) (clamped to [0, 14]),
   uniform 3-bit mantissa, never the NaN code; with the 1/128 scale about half the
   magnitudes fall in [1, 1.875).
 * every slot that holds no history before the step (unused pool blocks, tails of
@@ -172,7 +172,9 @@ def _fp8_codes(shape, device, seed):
     g = _gen(device, seed)
     sign = torch.randint(0, 2, shape, generator=g, device=device, dtype=torch.int32)
     geo = torch.empty(shape, device=device, dtype=torch.float32).geometric_(0.5, generator=g)
-    exp_field = (15 - geo.to(torch.int32)).clamp_(min=0)
+    # geometric_ can return 0 (its uniform draw may be exactly 1), so clamp both ends:
+    # exponent field 14 at most keeps every code finite (0x7F/0xFF are NaN).
+    exp_field = (15 - geo.to(torch.int32)).clamp_(min=0, max=14)
     mant = torch.randint(0, 8, shape, generator=g, device=device, dtype=torch.int32)
     return ((sign << 7) | (exp_field << 3) | mant).to(torch.uint8)
 
