@@ -2,7 +2,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/pkv.h"
+#include "pkv.h"
 #include "pkv_launch.h"
 
 

@@ -76,30 +76,15 @@ struct Tile {
   u32x4 v[MfmaTraits<QT, KVT, D>::kLoads];
 };
 
-template <int QT, int KVT, int D>
-__global__ __launch_bounds__(64) void paged_decode_mfma(DecodeArgs a) {
+// One work item: the G query heads of kv head it.g of sequence it.s over context
+// partition it.p, which holds tokens [start, ctx) up to the partition's end.
+template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO>
+__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, const int ctx, const int start,
+                                          int* bt_lds, uint8_t (*v_lds)[MfmaTraits<QT, KVT, D>::kVLdsBytes]) {
   using Tr = MfmaTraits<QT, KVT, D>;
-  extern __shared__ int bt_lds[];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][Tr::kVLdsBytes];
-
-  const int j = item_of_workgroup(blockIdx.x);
-  if (j >= a.num_items) return;
-  const Item it = decode_item(j, a);
   const int lane = threadIdx.x, n = lane & 15, j4 = lane >> 4;
   const int G = a.group;
-  const int ctx = min(a.context_lens[it.s], a.max_blocks * kBlock);
-  const int start = it.p * a.part_blocks * kBlock;
   const int head = it.g * G + n;
-
-  if (ctx <= start) {
-    // Nothing in this partition. A whole sequence with no context writes zeros.
-    if (a.num_parts == 1 && n < G) {
-      uint16_t* o = (uint16_t*)a.out + ((int64_t)it.s * a.num_q_heads + head) * D;
-#pragma unroll
-      for (int c = 0; c < Tr::kPv; ++c) *(u32x2*)(o + 16 * c + 4 * j4) = u32x2{0u, 0u};
-    }
-    return;
-  }
   const int end = min(ctx, start + a.part_blocks * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
 
@@ -143,9 +128,9 @@ __global__ __launch_bounds__(64) void paged_decode_mfma(DecodeArgs a) {
     const auto rk = make_rsrc(kbase + phys * block_stride, bytes);
     const auto rv = make_rsrc(vbase + phys * block_stride, bytes);
 #pragma unroll
-    for (int u = 0; u < Tr::kLoads; ++u) t.k[u] = buf_load16(rk, koff[u]);
+    for (int u = 0; u < Tr::kLoads; ++u) t.k[u] = buf_load16<POLICY>(rk, koff[u]);
 #pragma unroll
-    for (int u = 0; u < Tr::kLoads; ++u) t.v[u] = buf_load16(rv, voff[u]);
+    for (int u = 0; u < Tr::kLoads; ++u) t.v[u] = buf_load16<POLICY>(rv, voff[u]);
   };
 
   f32x4 o[Tr::kPv];
@@ -227,18 +212,20 @@ __global__ __launch_bounds__(64) void paged_decode_mfma(DecodeArgs a) {
     }
   };
 
-  Tile<QT, KVT, D> t0, t1;
-  load(t0, 0);
-  load(t1, 1);
-  // Two tiles in flight. The loop body has no branch around a load, so the waitcnt
-  // counts stay exact; when nblk is odd the last step processes a block past the end,
-  // which is harmless: its loads return zeros and every one of its tokens is masked
-  // (alpha = 1, p = 0).
-  for (int i = 0; i < nblk; i += 2) {
-    process(t0, i, v_lds[0]);
-    load(t0, i + 2);
-    process(t1, i + 1, v_lds[1]);
-    load(t1, i + 3);
+  // NBUF tiles in flight, kept in a ring of register tiles. The loop body has no branch
+  // around a load, so the waitcnt counts stay exact; when nblk is not a multiple of NBUF
+  // the last round processes blocks past the end, which is harmless: their loads return
+  // zeros and every one of their tokens is masked (alpha = 1, p = 0).
+  Tile<QT, KVT, D> t[NBUF];
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) load(t[b], b);
+  for (int i = 0; i < nblk; i += NBUF) {
+    if constexpr (PRIO) progress_priority(i, nblk);
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      process(t[b], i + b, v_lds[b & 1]);
+      load(t[b], i + b + NBUF);
+    }
   }
 
   const float l_tot = sum_xor32(sum_xor16(l_run));
@@ -259,6 +246,38 @@ __global__ __launch_bounds__(64) void paged_decode_mfma(DecodeArgs a) {
     for (int c = 0; c < Tr::kPv; ++c) *(f32x4*)(po + 16 * c + 4 * j4) = o[c];
     if (j4 == 0) *(f32x2*)(a.part_ml + prow * 2) = f32x2{m_run, l_tot};
   }
+}
+
+template <int QT, int KVT, int D>
+__global__ __launch_bounds__(64) void paged_decode_mfma(DecodeArgs a) {
+  using Tr = MfmaTraits<QT, KVT, D>;
+  extern __shared__ int bt_lds[];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][Tr::kVLdsBytes];
+
+  const int j = item_of_workgroup(blockIdx.x);
+  if (j >= a.num_items) return;
+  const Item it = decode_item(j, a);
+  const int ctx = min(a.context_lens[it.s], a.max_blocks * kBlock);
+  const int start = it.p * a.part_blocks * kBlock;
+  if (ctx <= start) {
+    // Nothing in this partition. A whole sequence with no context writes zeros.
+    const int n = threadIdx.x & 15, j4 = threadIdx.x >> 4;
+    if (a.num_parts == 1 && n < a.group) {
+      uint16_t* o = (uint16_t*)a.out + ((int64_t)it.s * a.num_q_heads + it.g * a.group + n) * D;
+#pragma unroll
+      for (int c = 0; c < Tr::kPv; ++c) *(u32x2*)(o + 16 * c + 4 * j4) = u32x2{0u, 0u};
+    }
+    return;
+  }
+  // Blocks shared with a neighbouring sequence: cached loads, two tiles in flight, default
+  // priority. Private blocks stream; a whole context in one partition does best with one
+  // tile in flight per wave, a split context (more items than wave slots) with two.
+  if (neighbour_shares_block(a, it.s, start / kBlock))
+    mfma_item<QT, KVT, D, 2, kPolicyCached, false>(a, it, ctx, start, bt_lds, v_lds);
+  else if (a.num_parts > 1)
+    mfma_item<QT, KVT, D, 2, kPolicyStream, true>(a, it, ctx, start, bt_lds, v_lds);
+  else
+    mfma_item<QT, KVT, D, 1, kPolicyStream, true>(a, it, ctx, start, bt_lds, v_lds);
 }
 
 template <int QT, int KVT, int D>

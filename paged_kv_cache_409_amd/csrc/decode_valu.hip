@@ -6,13 +6,15 @@
 // 维度一.3 公式 3-4). With a single query row per kv head there is no dense
 // contraction to give the matrix cores, so the work stays on the VALU:
 // * one wavefront per (sequence, kv head, context partition), block-table slice in LDS;
-// * per 16-token block each lane owns one token row (lane >> 2) and a quarter of its
-//   head_dim (lane & 3): 16-byte loads, dot2 instructions for q.k, then a DPP
-//   quad butterfly completes each token's dot product;
-// * online softmax: block max over the 16 tokens with DPP row rotations plus
+// * each 16-byte load instruction reads whole rows of the block's tile (one contiguous
+//   KiB), so lane l always holds the same column slice of head_dim, taken from a
+//   different token row in each load; q and the output accumulators are that one slice;
+// * q.k with dot2 instructions, then a DPP butterfly over the lanes of a row finishes each
+//   token's dot product;
+// * online softmax: block max and sum across the row groups with DPP row rotations and
 //   permlane16/32 swaps; exp2 with log2 e folded into the scale;
-// * each lane accumulates p * V for its token and columns; the 16 token partial
-//   sums are combined once at the end of the partition.
+// * each lane accumulates p * V for its rows and columns; the row groups are combined
+//   once at the end of the partition.
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -21,21 +23,50 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
-constexpr int kRowRor4 = 0x124;   // row_ror:4
-constexpr int kRowRor8 = 0x128;   // row_ror:8
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane l <-> 7 - l within each 8 lanes
+constexpr int kRowMirror = 0x140;      // lane l <-> 15 - l within each 16 lanes
+constexpr int kRowRor4 = 0x124;        // row_ror:4
+constexpr int kRowRor8 = 0x128;        // row_ror:8
 
-// Reduce over the 16 token rows (lane bits 2..5) of the wave.
-__device__ __forceinline__ float sum_tokens(float x) {
-  x += dpp<kRowRor4>(x);
-  x += dpp<kRowRor8>(x);
-  return sum_xor32(sum_xor16(x));
+// K+V tiles each wavefront keeps in flight (one measured best on gfx950: the two waves
+// of a SIMD already overlap each other's loads).
+constexpr int kValuTilesInFlight = 1;
+
+template <int QT, int KVT, int D>
+struct ValuTraits {
+  static constexpr int kElem = (KVT == kFP8) ? 1 : 2;
+  static constexpr int kTileBytes = kBlock * D * kElem;     // one kv head's slice of a block
+  static constexpr int kLoads = kTileBytes / (16 * kWave);  // 16-byte loads per lane per tile
+  static constexpr int kLanesPerRow = D * kElem / 16;       // lanes sharing one token row
+  static constexpr int kRowsPerLoad = kWave / kLanesPerRow; // token rows one load covers
+  static constexpr int kCols = 16 / kElem;                  // head_dim columns per lane
+  static constexpr int kWords = kCols / 2;                  // packed 16-bit pairs per lane
+};
+
+// Sum over the kLanesPerRow consecutive lanes holding one row (the result lands in all).
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  if constexpr (LPR >= 8) x += dpp<kRowHalfMirror>(x);
+  if constexpr (LPR >= 16) x += dpp<kRowMirror>(x);
+  return x;
 }
-__device__ __forceinline__ float max_tokens(float x) {
-  x = fmaxf(x, dpp<kRowRor4>(x));
-  x = fmaxf(x, dpp<kRowRor8>(x));
+
+// Max / sum across the row groups: over all lanes that share l % LPR.
+template <int LPR>
+__device__ __forceinline__ float groups_max(float x) {
+  if constexpr (LPR <= 4) x = fmaxf(x, dpp<kRowRor4>(x));
+  if constexpr (LPR <= 8) x = fmaxf(x, dpp<kRowRor8>(x));
   return max_xor32(max_xor16(x));
+}
+template <int LPR>
+__device__ __forceinline__ float groups_sum(float x) {
+  if constexpr (LPR <= 4) x += dpp<kRowRor4>(x);
+  if constexpr (LPR <= 8) x += dpp<kRowRor8>(x);
+  return sum_xor32(sum_xor16(x));
 }
 
 template <int QT>
@@ -47,20 +78,19 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
 }
 
-template <int QT, int KVT, int D>
-struct ValuTraits {
-  static constexpr int kElem = (KVT == kFP8) ? 1 : 2;
-  static constexpr int kTileBytes = kBlock * D * kElem;
-  static constexpr int kLoads = kTileBytes / (16 * kWave);   // 16-byte loads per lane per tile
-  static constexpr int kPerLoad = 16 / kElem;                // elements per load
-  static constexpr int kCols = D / 4;                        // head_dim columns per lane
-};
-
-// Column of the e-th element of load u for quarter q4: loads cover 16 bytes of the
-// row each, quarters interleaved so that one instruction reads 64 contiguous bytes per row.
-template <int KVT>
-__device__ __forceinline__ int valu_col(int u, int q4) {
-  return (KVT == kFP8 ? 16 : 8) * (4 * u + q4);
+// One 16-byte load as packed 16-bit pairs of the q dtype (fp8 codes widen exactly).
+template <int QT, int KVT>
+__device__ __forceinline__ void widen(const u32x4& w, uint32_t* dst) {
+  if constexpr (KVT == kFP8) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const u32x2 h = fp8x4_to_16<QT>(w[x]);
+      dst[2 * x] = h[0];
+      dst[2 * x + 1] = h[1];
+    }
+  } else {
+    dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
+  }
 }
 
 template <int QT, int KVT, int D>
@@ -69,30 +99,15 @@ struct VTile {
   u32x4 v[ValuTraits<QT, KVT, D>::kLoads];
 };
 
-template <int QT, int KVT, int D>
-__global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
+// One work item: query head it.g of sequence it.s over context partition it.p, which
+// holds tokens [start, ctx) up to the partition's end.
+template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO>
+__device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, const int ctx, const int start,
+                                          int* bt_lds) {
   using Tr = ValuTraits<QT, KVT, D>;
-  extern __shared__ int bt_lds[];
-
-  const int j = item_of_workgroup(blockIdx.x);
-  if (j >= a.num_items) return;
-  const Item it = decode_item(j, a);
-  const int lane = threadIdx.x, tr = lane >> 2, q4 = lane & 3;
-  const int ctx = min(a.context_lens[it.s], a.max_blocks * kBlock);
-  const int start = it.p * a.part_blocks * kBlock;
+  constexpr int LPR = Tr::kLanesPerRow, RPL = Tr::kRowsPerLoad;
+  const int lane = threadIdx.x, grp = lane / LPR, col0 = (lane % LPR) * Tr::kCols;
   const int head = it.g;   // one query head per kv head
-
-  if (ctx <= start) {
-    if (a.num_parts == 1 && tr == 0) {
-      uint8_t* o = (uint8_t*)((uint16_t*)a.out + ((int64_t)it.s * a.num_q_heads + head) * D);
-#pragma unroll
-      for (int u = 0; u < Tr::kLoads; ++u) {
-        const int c0 = valu_col<KVT>(u, q4);
-        for (int e = 0; e < Tr::kPerLoad; e += 8) *(u32x4*)(o + (c0 + e) * 2) = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    return;
-  }
   const int end = min(ctx, start + a.part_blocks * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
   {
@@ -100,44 +115,35 @@ __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
     for (int i = lane; i < nblk; i += kWave) bt_lds[i] = bt[i];
   }
 
-  // q for this lane's columns, packed 16-bit pairs (same order as the K elements).
-  uint32_t qv[Tr::kCols / 2];
+  // q columns [col0, col0 + kCols) as packed 16-bit pairs.
+  uint32_t qv[Tr::kWords];
   {
-    const uint8_t* qrow = (const uint8_t*)((const uint16_t*)a.q + (int64_t)it.s * a.q_seq_stride +
-                                           (int64_t)head * D);
+    const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)it.s * a.q_seq_stride + (int64_t)head * D + col0;
 #pragma unroll
-    for (int u = 0; u < Tr::kLoads; ++u) {
-      const int c0 = valu_col<KVT>(u, q4);
-#pragma unroll
-      for (int e = 0; e < Tr::kPerLoad; e += 8) {
-        const u32x4 w = *(const u32x4*)(qrow + (c0 + e) * 2);
-        const int base = (u * Tr::kPerLoad + e) / 2;
-        qv[base + 0] = w[0]; qv[base + 1] = w[1]; qv[base + 2] = w[2]; qv[base + 3] = w[3];
-      }
+    for (int x = 0; x < Tr::kWords; x += 4) {
+      const u32x4 w = *(const u32x4*)(qrow + 2 * x);
+      qv[x] = w[0]; qv[x + 1] = w[1]; qv[x + 2] = w[2]; qv[x + 3] = w[3];
     }
   }
   __syncthreads();
-
-  uint32_t off[Tr::kLoads];
-#pragma unroll
-  for (int u = 0; u < Tr::kLoads; ++u) off[u] = tr * D * Tr::kElem + valu_col<KVT>(u, q4) * Tr::kElem;
 
   const int64_t head_stride = (int64_t)Tr::kTileBytes;
   const uint8_t* kbase = (const uint8_t*)a.k_cache + (int64_t)it.g * head_stride;
   const uint8_t* vbase = (const uint8_t*)a.v_cache + (int64_t)it.g * head_stride;
   const int64_t block_stride = (int64_t)a.num_kv_heads * head_stride;
+  const uint32_t off0 = lane * 16;
 
   auto load = [&](VTile<QT, KVT, D>& t, int i) {
     const int id = readfirstlane(i < nblk ? bt_lds[i < nblk ? i : 0] : -1);
     const bool live = id >= 0 && id < a.num_blocks;
     const int phys = live ? id : 0;
-    const uint32_t bytes = live ? (uint32_t)Tr::kTileBytes : 0u;
+    const uint32_t bytes = live ? (uint32_t)Tr::kTileBytes : 0u;   // 0: loads return zeros
     const auto rk = make_rsrc(kbase + phys * block_stride, bytes);
     const auto rv = make_rsrc(vbase + phys * block_stride, bytes);
 #pragma unroll
-    for (int u = 0; u < Tr::kLoads; ++u) t.k[u] = buf_load16(rk, off[u]);
+    for (int u = 0; u < Tr::kLoads; ++u) t.k[u] = buf_load16<POLICY>(rk, off0 + u * 1024);
 #pragma unroll
-    for (int u = 0; u < Tr::kLoads; ++u) t.v[u] = buf_load16(rv, off[u]);
+    for (int u = 0; u < Tr::kLoads; ++u) t.v[u] = buf_load16<POLICY>(rv, off0 + u * 1024);
   };
 
   float o[Tr::kCols];
@@ -146,110 +152,118 @@ __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float qk_scale = a.qk_scale_log2;
 
-  // Packed 16-bit view of one loaded dword pair-list: for fp8 each dword widens to two.
-  auto widen = [&](const u32x4& w, uint32_t* dst) {
-    if constexpr (KVT == kFP8) {
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const u32x2 h = fp8x4_to_16<QT>(w[x]);
-        dst[2 * x] = h[0];
-        dst[2 * x + 1] = h[1];
-      }
-    } else {
-      dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
-    }
-  };
-  constexpr int kWords = Tr::kPerLoad / 2;   // packed pairs per load after widening
-
   auto process = [&](const VTile<QT, KVT, D>& t, int i) {
-    float dot = 0.f;
+    float sc[Tr::kLoads];
+    bool valid[Tr::kLoads];
 #pragma unroll
     for (int u = 0; u < Tr::kLoads; ++u) {
-      uint32_t kw[kWords];
-      widen(t.k[u], kw);
+      uint32_t kw[Tr::kWords];
+      widen<QT, KVT>(t.k[u], kw);
+      float dot = 0.f;
 #pragma unroll
-      for (int x = 0; x < kWords; ++x) dot = dot2<QT>(kw[x], qv[u * kWords + x], dot);
+      for (int x = 0; x < Tr::kWords; ++x) dot = dot2<QT>(kw[x], qv[x], dot);
+      dot = row_sum<LPR>(dot);
+      valid[u] = start + i * kBlock + u * RPL + grp < end;   // inside this partition and the context
+      sc[u] = valid[u] ? dot * qk_scale : -INFINITY;
     }
-    dot += dpp<kQuadXor1>(dot);
-    dot += dpp<kQuadXor2>(dot);
-    const bool valid = start + i * kBlock + tr < end;   // inside this partition and the context
-    const float sc = valid ? dot * qk_scale : -INFINITY;
-    const float m_new = fmaxf(m_run, max_tokens(sc));
+    float mb = sc[0];
+#pragma unroll
+    for (int u = 1; u < Tr::kLoads; ++u) mb = fmaxf(mb, sc[u]);
+    const float m_new = fmaxf(m_run, groups_max<LPR>(mb));
     const float alpha = exp2_fast(m_run - m_new);
     m_run = m_new;
-    const float p = exp2_fast(sc - m_new);
-    l_run = l_run * alpha + p;
+    float p[Tr::kLoads], psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < Tr::kLoads; ++u) {
+      p[u] = exp2_fast(sc[u] - m_new);
+      psum += p[u];
+    }
+    l_run = l_run * alpha + psum;
     if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int c = 0; c < Tr::kCols; ++c) o[c] *= alpha;
     }
 #pragma unroll
     for (int u = 0; u < Tr::kLoads; ++u) {
-      uint32_t vw[kWords];
-      widen(valid ? t.v[u] : u32x4{0u, 0u, 0u, 0u}, vw);
+      uint32_t vw[Tr::kWords];
+      widen<QT, KVT>(valid[u] ? t.v[u] : u32x4{0u, 0u, 0u, 0u}, vw);   // stale rows never multiply
 #pragma unroll
-      for (int x = 0; x < kWords; ++x) {
-        const int c = u * Tr::kPerLoad + 2 * x;
-        o[c] = fmaf(p, lo16<QT>(vw[x]), o[c]);
-        o[c + 1] = fmaf(p, hi16<QT>(vw[x]), o[c + 1]);
+      for (int x = 0; x < Tr::kWords; ++x) {
+        o[2 * x] = fmaf(p[u], lo16<QT>(vw[x]), o[2 * x]);
+        o[2 * x + 1] = fmaf(p[u], hi16<QT>(vw[x]), o[2 * x + 1]);
       }
     }
   };
 
-  VTile<QT, KVT, D> t0, t1;
-  load(t0, 0);
-  load(t1, 1);
-  // Two tiles in flight; see the matrix-core kernel for why a block past the end is
-  // processed when nblk is odd (zero loads, all tokens masked, no effect).
-  for (int i = 0; i < nblk; i += 2) {
-    process(t0, i);
-    load(t0, i + 2);
-    process(t1, i + 1);
-    load(t1, i + 3);
+  // NBUF tiles in flight in a ring of register tiles; see the matrix-core kernel for why
+  // blocks past the end may be processed (zero loads, all tokens masked, no effect).
+  VTile<QT, KVT, D> t[NBUF];
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) load(t[b], b);
+  for (int i = 0; i < nblk; i += NBUF) {
+    if constexpr (PRIO) progress_priority(i, nblk);
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      process(t[b], i + b);
+      load(t[b], i + b + NBUF);
+    }
   }
 
-  // Combine the 16 token rows.
-  const float l_tot = sum_tokens(l_run);
+  // Combine the row groups.
+  const float l_tot = groups_sum<LPR>(l_run);
 #pragma unroll
-  for (int c = 0; c < Tr::kCols; ++c) o[c] = sum_tokens(o[c]);
-  if (tr != 0) return;
+  for (int c = 0; c < Tr::kCols; ++c) o[c] = groups_sum<LPR>(o[c]);
+  if (grp != 0) return;
   const int64_t row = (int64_t)it.s * a.num_q_heads + head;
   if (a.num_parts == 1) {
     const float inv = a.v_scale / l_tot;
-    uint8_t* orow = (uint8_t*)((uint16_t*)a.out + row * D);
+    uint16_t* orow = (uint16_t*)a.out + row * D + col0;
 #pragma unroll
-    for (int u = 0; u < Tr::kLoads; ++u) {
-      const int c0 = valu_col<KVT>(u, q4);
+    for (int x = 0; x < Tr::kWords; x += 4) {
+      u32x4 w;
 #pragma unroll
-      for (int e = 0; e < Tr::kPerLoad; e += 8) {
-        const int c = u * Tr::kPerLoad + e;
-        u32x4 w;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) w[x] = pack2<QT>(o[c + 2 * x] * inv, o[c + 2 * x + 1] * inv);
-        *(u32x4*)(orow + (c0 + e) * 2) = w;
-      }
+      for (int y = 0; y < 4; ++y) w[y] = pack2<QT>(o[2 * (x + y)] * inv, o[2 * (x + y) + 1] * inv);
+      *(u32x4*)(orow + 2 * x) = w;
     }
   } else {
     const int64_t prow = row * a.num_parts + it.p;
-    float* po = a.part_o + prow * D;
+    float* po = a.part_o + prow * D + col0;
 #pragma unroll
-    for (int u = 0; u < Tr::kLoads; ++u) {
-      const int c0 = valu_col<KVT>(u, q4);
-#pragma unroll
-      for (int e = 0; e < Tr::kPerLoad; e += 4) {
-        const int c = u * Tr::kPerLoad + e;
-        *(f32x4*)(po + c0 + e) = f32x4{o[c], o[c + 1], o[c + 2], o[c + 3]};
-      }
-    }
-    if (q4 == 0) *(f32x2*)(a.part_ml + prow * 2) = f32x2{m_run, l_tot};
+    for (int c = 0; c < Tr::kCols; c += 4) *(f32x4*)(po + c) = f32x4{o[c], o[c + 1], o[c + 2], o[c + 3]};
+    if (lane == 0) *(f32x2*)(a.part_ml + prow * 2) = f32x2{m_run, l_tot};
   }
+}
+
+template <int QT, int KVT, int D, int NBUF>
+__global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
+  using Tr = ValuTraits<QT, KVT, D>;
+  extern __shared__ int bt_lds[];
+  const int j = item_of_workgroup(blockIdx.x);
+  if (j >= a.num_items) return;
+  const Item it = decode_item(j, a);
+  const int ctx = min(a.context_lens[it.s], a.max_blocks * kBlock);
+  const int start = it.p * a.part_blocks * kBlock;
+  if (ctx <= start) {
+    // Nothing in this partition. A whole sequence with no context writes zeros.
+    const int lane = threadIdx.x;
+    if (a.num_parts == 1 && lane < Tr::kLanesPerRow) {
+      uint16_t* o = (uint16_t*)a.out + ((int64_t)it.s * a.num_q_heads + it.g) * D + lane * Tr::kCols;
+#pragma unroll
+      for (int x = 0; x < Tr::kCols; x += 8) *(u32x4*)(o + x) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
+  if (neighbour_shares_block(a, it.s, start / kBlock))
+    valu_item<QT, KVT, D, NBUF, kPolicyCached, false>(a, it, ctx, start, bt_lds);
+  else
+    valu_item<QT, KVT, D, NBUF, kPolicyStream, true>(a, it, ctx, start, bt_lds);
 }
 
 template <int QT, int KVT, int D>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int grid = (a.num_items + 31) / 32 * 32;
   const size_t lds = (size_t)a.part_blocks * sizeof(int);
-  hipLaunchKernelGGL((paged_decode_valu<QT, KVT, D>), dim3(grid), dim3(kWave), lds, stream, a);
+  hipLaunchKernelGGL((paged_decode_valu<QT, KVT, D, kValuTilesInFlight>), dim3(grid), dim3(kWave), lds, stream, a);
   return hipGetLastError();
 }
 
