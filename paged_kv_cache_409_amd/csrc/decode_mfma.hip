@@ -35,8 +35,9 @@ struct MfmaTraits {
   static constexpr int kQk = D / 32;                    // 16x16x32 steps per block (QK)
   static constexpr int kPv = D / 16;                    // 16x16x16 steps per block (PV)
   static constexpr int kLoads = kTileBytes / (16 * kWave);  // 16-byte loads per lane per tile
-  static constexpr int kRowChunks = D / 8;              // 16-byte chunks per 16-bit V row
-  static constexpr int kVLdsBytes = kBlock * D * 2;     // V tile in LDS, 16-bit elements
+  static constexpr int kRowChunks = D / 8;              // 16-byte chunks per 16-bit row in LDS
+  static constexpr int kTileLds = kBlock * D * 2;       // one tile in LDS, 16-bit elements
+  static constexpr int kLdsBytes = 2 * kTileLds;        // K tile, then V tile
 };
 
 template <int QT>
@@ -58,10 +59,19 @@ __device__ __forceinline__ f32x4 mfma_pv(i16x4 a, u32x2 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
-// Element index d (within the head) that lane row j4 feeds as k-slot 8*j4..8*j4+7 of QK
-// step c. The contraction order is free, so the map is chosen to make each lane's
-// K bytes contiguous: 16-bit caches use d = 32c + 8*j4 + i; an fp8 cache pairs
-// steps (2h, 2h+1) on one 16-byte load: d = 64h + 16*j4 + 8*(c&1) + i.
+// Element index d (within the head) that lane row j4 feeds as k-slots 8*j4..8*j4+7 of QK
+// step c. The contraction order is free; it is fixed per cache dtype so that every way of
+// reading K gives the same sums, bit for bit:
+// * 16-bit caches: d = 32c + 8*j4 + i;
+// * fp8 caches pair steps (2h, 2h+1) on one 16-byte load of 16 codes:
+//   d = 64h + 16*j4 + 8*(c&1) + i.
+// K reaches the matrix cores in one of two ways:
+// * through LDS: the tile is loaded from HBM with whole rows per instruction (each 16-byte
+//   load instruction covers one contiguous KiB), widened to 16-bit if it is fp8, stored
+//   XOR-swizzled, and each lane reads its A-operand fragment (row n, elements d..d+7) as one
+//   16-byte LDS read;
+// * straight into registers: lane (n, j4) loads its own fragment of row n, so one load
+//   instruction covers 16 rows x 64 bytes.
 template <int KVT>
 __device__ __forceinline__ int qk_d0(int c, int j4) {
   if constexpr (KVT == kFP8)
@@ -78,9 +88,9 @@ struct Tile {
 
 // One work item: the G query heads of kv head it.g of sequence it.s over context
 // partition it.p, which holds tokens [start, ctx) up to the partition's end.
-template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO>
+template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO, bool KLDS>
 __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, const int ctx, const int start,
-                                          int* bt_lds, uint8_t (*v_lds)[MfmaTraits<QT, KVT, D>::kVLdsBytes]) {
+                                          int* bt_lds, uint8_t (*kv_lds)[MfmaTraits<QT, KVT, D>::kLdsBytes]) {
   using Tr = MfmaTraits<QT, KVT, D>;
   const int lane = threadIdx.x, n = lane & 15, j4 = lane >> 4;
   const int G = a.group;
@@ -104,15 +114,19 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, co
   }
   __syncthreads();
 
-  // Per-lane byte offsets inside one kv head's tile.
+  // Per-lane byte offsets inside one kv head's tile. V (and K through LDS): lane l reads
+  // bytes [16 (64 u + l), +16) with load u, one contiguous KiB per instruction. K straight
+  // into registers: lane (n, j4) reads its own fragment of row n.
   uint32_t koff[Tr::kLoads], voff[Tr::kLoads];
 #pragma unroll
   for (int u = 0; u < Tr::kLoads; ++u) {
-    if constexpr (KVT == kFP8)
+    voff[u] = (u * kWave + lane) * 16;
+    if constexpr (KLDS)
+      koff[u] = voff[u];
+    else if constexpr (KVT == kFP8)
       koff[u] = n * D + 64 * u + 16 * j4;                       // row n, 16 fp8 values
     else
-      koff[u] = (n * D + qk_d0<KVT>(u, j4)) * 2;                // row n, 8 values
-    voff[u] = (u * kWave + lane) * 16;                           // contiguous pieces
+      koff[u] = (n * D + qk_d0<KVT>(u, j4)) * 2;          // row n, 8 values
   }
 
   const int64_t head_stride = (int64_t)Tr::kTileBytes;
@@ -139,13 +153,49 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, co
   float m_run = -INFINITY, l_run = 0.f;
   const float qk_scale = a.qk_scale_log2;
 
-  auto process = [&](const Tile<QT, KVT, D>& t, int i, uint8_t* vl) {
+  // A tile -> LDS as 16-bit rows; chunk k of row r is stored at k ^ (r mod chunks). Rows
+  // at or past `valid_rows` are stored as zeros when `mask` is set.
+  auto stage = [&](const u32x4* w_in, uint8_t* dst, bool mask, int valid_rows) {
+#pragma unroll
+    for (int u = 0; u < Tr::kLoads; ++u) {
+      const int f = u * kWave + lane;
+      if constexpr (KVT == kFP8) {
+        const int r = f / (D / 16), ch = f % (D / 16);
+        u32x4 w = w_in[u];
+        if (mask && r >= valid_rows) w = u32x4{0u, 0u, 0u, 0u};
+        const u32x2 a0 = fp8x4_to_16<QT>(w[0]), a1 = fp8x4_to_16<QT>(w[1]);
+        const u32x2 a2 = fp8x4_to_16<QT>(w[2]), a3 = fp8x4_to_16<QT>(w[3]);
+        const int sw = r & (Tr::kRowChunks - 1);
+        *(u32x4*)(dst + (r * Tr::kRowChunks + ((2 * ch) ^ sw)) * 16) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        *(u32x4*)(dst + (r * Tr::kRowChunks + ((2 * ch + 1) ^ sw)) * 16) = u32x4{a2[0], a2[1], a3[0], a3[1]};
+      } else {
+        const int r = f / Tr::kRowChunks, ch = f % Tr::kRowChunks;
+        u32x4 w = w_in[u];
+        if (mask && r >= valid_rows) w = u32x4{0u, 0u, 0u, 0u};
+        *(u32x4*)(dst + (r * Tr::kRowChunks + (ch ^ (r & (Tr::kRowChunks - 1)))) * 16) = w;
+      }
+    }
+  };
+
+  auto process = [&](const Tile<QT, KVT, D>& t, int i, uint8_t* lds) {
+    uint8_t* kl = lds;
+    uint8_t* vl = lds + Tr::kTileLds;
+    // K rows past the partition are not masked here: their scores are replaced by -inf.
+    // V rows past it are zeroed, since 0 * stale NaN would poison the product.
+    const int valid_rows = end - start - i * kBlock;
+    if constexpr (KLDS) stage(t.k, kl, false, 0);
+    stage(t.v, vl, valid_rows < kBlock, valid_rows);
+    __syncthreads();
+
     // S^T = K . Q^T for this block.
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < Tr::kQk; ++c) {
       u32x4 ka;
-      if constexpr (KVT == kFP8) {
+      if constexpr (KLDS) {
+        const int ch = qk_d0<KVT>(c, j4) >> 3;   // 16-byte chunk of 8 16-bit elements
+        ka = *(const u32x4*)(kl + (n * Tr::kRowChunks + (ch ^ (n & (Tr::kRowChunks - 1)))) * 16);
+      } else if constexpr (KVT == kFP8) {
         const u32x4 w = t.k[c >> 1];
         const u32x2 lo = fp8x4_to_16<QT>(w[(c & 1) * 2]);
         const u32x2 hi = fp8x4_to_16<QT>(w[(c & 1) * 2 + 1]);
@@ -175,29 +225,6 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, co
       for (int c = 0; c < Tr::kPv; ++c) o[c] *= alpha;
     }
 
-    // V tile -> LDS (16-bit elements, chunk k of row r stored at k ^ (r mod chunks)).
-    const bool tail = (i * kBlock + kBlock) > (end - start);   // block holds slots past the partition
-#pragma unroll
-    for (int u = 0; u < Tr::kLoads; ++u) {
-      const int f = u * kWave + lane;
-      if constexpr (KVT == kFP8) {
-        const int r = f / (D / 16), ch = f % (D / 16);
-        u32x4 w = t.v[u];
-        if (tail && start + i * kBlock + r >= end) w = u32x4{0u, 0u, 0u, 0u};
-        const u32x2 a0 = fp8x4_to_16<QT>(w[0]), a1 = fp8x4_to_16<QT>(w[1]);
-        const u32x2 a2 = fp8x4_to_16<QT>(w[2]), a3 = fp8x4_to_16<QT>(w[3]);
-        const int sw = r & (Tr::kRowChunks - 1);
-        *(u32x4*)(vl + (r * Tr::kRowChunks + ((2 * ch) ^ sw)) * 16) = u32x4{a0[0], a0[1], a1[0], a1[1]};
-        *(u32x4*)(vl + (r * Tr::kRowChunks + ((2 * ch + 1) ^ sw)) * 16) = u32x4{a2[0], a2[1], a3[0], a3[1]};
-      } else {
-        const int r = f / Tr::kRowChunks, ch = f % Tr::kRowChunks;
-        u32x4 w = t.v[u];
-        if (tail && start + i * kBlock + r >= end) w = u32x4{0u, 0u, 0u, 0u};
-        *(u32x4*)(vl + (r * Tr::kRowChunks + (ch ^ (r & (Tr::kRowChunks - 1)))) * 16) = w;
-      }
-    }
-    __syncthreads();
-
     // O^T += V^T . P
     const u32x2 pb = {p01, p23};
     const int rr = 4 * j4 + (n >> 2);
@@ -223,7 +250,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, co
     if constexpr (PRIO) progress_priority(i, nblk);
 #pragma unroll
     for (int b = 0; b < NBUF; ++b) {
-      process(t[b], i + b, v_lds[b & 1]);
+      process(t[b], i + b, kv_lds[b & 1]);
       load(t[b], i + b + NBUF);
     }
   }
@@ -252,7 +279,7 @@ template <int QT, int KVT, int D>
 __global__ __launch_bounds__(64) void paged_decode_mfma(DecodeArgs a) {
   using Tr = MfmaTraits<QT, KVT, D>;
   extern __shared__ int bt_lds[];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][Tr::kVLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2][Tr::kLdsBytes];
 
   const int j = item_of_workgroup(blockIdx.x);
   if (j >= a.num_items) return;
@@ -269,15 +296,17 @@ __global__ __launch_bounds__(64) void paged_decode_mfma(DecodeArgs a) {
     }
     return;
   }
-  // Blocks shared with a neighbouring sequence: cached loads, two tiles in flight, default
-  // priority. Private blocks stream; a whole context in one partition does best with one
-  // tile in flight per wave, a split context (more items than wave slots) with two.
+  // Blocks shared with a neighbouring sequence: cached loads (the other readers hit L2),
+  // two tiles in flight, default priority, K straight into registers (these items are
+  // bound by per-block latency more than by HBM). Private blocks stream, with K through
+  // LDS; a whole context in one partition does best with one tile in flight per wave, a
+  // split context (more items than wave slots) with two.
   if (neighbour_shares_block(a, it.s, start / kBlock))
-    mfma_item<QT, KVT, D, 2, kPolicyCached, false>(a, it, ctx, start, bt_lds, v_lds);
+    mfma_item<QT, KVT, D, 2, kPolicyCached, false, false>(a, it, ctx, start, bt_lds, kv_lds);
   else if (a.num_parts > 1)
-    mfma_item<QT, KVT, D, 2, kPolicyStream, true>(a, it, ctx, start, bt_lds, v_lds);
+    mfma_item<QT, KVT, D, 2, kPolicyStream, true, true>(a, it, ctx, start, bt_lds, kv_lds);
   else
-    mfma_item<QT, KVT, D, 1, kPolicyStream, true>(a, it, ctx, start, bt_lds, v_lds);
+    mfma_item<QT, KVT, D, 1, kPolicyStream, true, true>(a, it, ctx, start, bt_lds, kv_lds);
 }
 
 template <int QT, int KVT, int D>

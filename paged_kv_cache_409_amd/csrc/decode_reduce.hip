@@ -9,38 +9,62 @@
 namespace pkv {
 
 
+// One workgroup of 256 threads per output row (sequence, q head). Thread (pg, cg) owns
+// columns 4cg..4cg+3 of every partition p = pg (mod kSlices); the kSlices partial sums
+// are added in LDS in a fixed order, so the result does not depend on timing.
 template <int QT, int D>
 __global__ __launch_bounds__(256) void paged_decode_reduce(ReduceArgs a) {
-  constexpr int kTpr = D / 4;              // threads per output row, 4 columns each
-  constexpr int kRows = 256 / kTpr;
-  const int row = blockIdx.x * kRows + threadIdx.x / kTpr;
-  const int col = (threadIdx.x % kTpr) * 4;
-  if (row >= a.num_seqs * a.num_q_heads) return;
+  constexpr int kGroups = D / 4;              // column groups of 4 floats
+  constexpr int kSlices = 256 / kGroups;      // partition slices
+  __shared__ float wave_max[256 / kWave];
+  __shared__ f32x4 part_acc[kSlices][kGroups];
+  __shared__ float part_l[kSlices];
+
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, cg = tid % kGroups, pg = tid / kGroups;
   const int s = row / a.num_q_heads;
   const int ctx = min(a.context_lens[s], a.max_tokens);
   const int np = min(ctx > 0 ? (ctx + a.part_tokens - 1) / a.part_tokens : 0, a.num_parts);
   const float* ml = a.part_ml + (int64_t)row * a.num_parts * 2;
-  const float* po = a.part_o + (int64_t)row * a.num_parts * D + col;
+  const float* po = a.part_o + (int64_t)row * a.num_parts * D + 4 * cg;
 
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  // M = max over the partitions' running maxima (log2 units).
+  float m = -INFINITY;
+  for (int p = tid; p < np; p += 256) m = fmaxf(m, ml[2 * p]);
+#pragma unroll
+  for (int x = kWave / 2; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x, kWave));
+  if ((tid & (kWave - 1)) == 0) wave_max[tid / kWave] = m;
+  __syncthreads();
+  float M = wave_max[0];
+#pragma unroll
+  for (int w = 1; w < 256 / kWave; ++w) M = fmaxf(M, wave_max[w]);
+
   float L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int p = 0; p < np; ++p) {
+  for (int p = pg; p < np; p += kSlices) {
     const float w = exp2_fast(ml[2 * p] - M);
     L = fmaf(w, ml[2 * p + 1], L);
     acc += w * *(const f32x4*)(po + (int64_t)p * D);
   }
-  const float inv = np > 0 ? a.v_scale / L : 0.f;
-  acc *= inv;
-  uint16_t* o = (uint16_t*)a.out + (int64_t)row * D + col;
-  *(u32x2*)o = u32x2{pack2<QT>(acc[0], acc[1]), pack2<QT>(acc[2], acc[3])};
+  part_acc[pg][cg] = acc;
+  if (cg == 0) part_l[pg] = L;
+  __syncthreads();
+  if (pg != 0) return;
+  f32x4 sum = part_acc[0][cg];
+  float Lsum = part_l[0];
+#pragma unroll
+  for (int q = 1; q < kSlices; ++q) {
+    sum += part_acc[q][cg];
+    Lsum += part_l[q];
+  }
+  const float inv = np > 0 ? a.v_scale / Lsum : 0.f;
+  sum *= inv;
+  uint16_t* o = (uint16_t*)a.out + (int64_t)row * D + 4 * cg;
+  *(u32x2*)o = u32x2{pack2<QT>(sum[0], sum[1]), pack2<QT>(sum[2], sum[3])};
 }
 
 hipError_t launch_decode_reduce(const ReduceArgs& a, int q_type, int head_dim, hipStream_t stream) {
-  const int rows = a.num_seqs * a.num_q_heads;
-  const int rows_per_wg = 256 / (head_dim / 4);
-  const dim3 grid((rows + rows_per_wg - 1) / rows_per_wg);
+  const dim3 grid(a.num_seqs * a.num_q_heads);
 #define PKV_CASE(QT, D)                                                                    \
   if (q_type == QT && head_dim == D) {                                                      \
     hipLaunchKernelGGL((paged_decode_reduce<QT, D>), grid, dim3(256), 0, stream, a);        \

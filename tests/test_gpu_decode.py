@@ -100,18 +100,20 @@ def test_output_is_bit_identical_under_block_permutation(G, dtype, kv_dtype):
     assert torch.equal(b_out.view(torch.int16), again.view(torch.int16))   # deterministic
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
-def test_shared_prefix_blocks_equal_private_copies(kv_dtype):
+@pytest.mark.parametrize("partition", [0, 64])
+@pytest.mark.parametrize("G,kv_dtype", [(4, "bf16"), (4, "fp8_e4m3"), (1, "bf16"), (1, "fp8_e4m3")])
+def test_shared_prefix_blocks_equal_private_copies(G, kv_dtype, partition):
     # Beams reading shared prefix blocks give bit-identical outputs to beams reading
-    # private copies of every block.
-    cfg = WorkloadConfig(name="beam_small", num_seqs=8, num_q_heads=8, num_kv_heads=2, head_dim=128,
+    # private copies of every block. (The kernels read shared and private blocks with
+    # different cache policies and pipelines; the arithmetic must not differ.)
+    cfg = WorkloadConfig(name="beam_small", num_seqs=8, num_q_heads=2 * G, num_kv_heads=2, head_dim=128,
                          num_blocks=1024, seed=11, dtype="bf16", kv_dtype=kv_dtype, ctx=("beam", 64, 0, 40, 4),
                          max_context_len=64 + 40 + 1, kv_scale=(1 / 128 if kv_dtype == "fp8_e4m3" else 1.0))
     b = device_batch(cfg)
     h = HostBatch(b)
     assert len(h.copy_pairs) > 0
-    say(cfg.name, kv_dtype, "shared vs private")
-    shared = gpu_step(b)
+    say(cfg.name, G, kv_dtype, "partition", partition, "shared vs private")
+    shared = gpu_step(b, partition)
     torch.cuda.synchronize()
     kc, vc = oracle_caches_after_step(h)
     assert max_err(shared, oracle_decode(h, kc, vc)) <= tol(cfg)
@@ -134,7 +136,7 @@ def test_shared_prefix_blocks_equal_private_copies(kv_dtype):
     b.k_cache[idx_d] = b.k_cache[idx_s]
     b.v_cache[idx_d] = b.v_cache[idx_s]
     b.block_tables = torch.from_numpy(new_bt).cuda()
-    private = gpu_decode(b)
+    private = gpu_decode(b, partition_size=partition)
     torch.cuda.synchronize()
     assert torch.equal(shared.view(torch.int16), private.view(torch.int16))
 
