@@ -12,6 +12,7 @@ constexpr int kMaxGroup = 16;
 constexpr int kMaxPartTokens = 32768;     // block-table slice of one partition: 2048 ids in LDS
 constexpr int kTargetItems = 2048;        // about two resident wavefronts per SIMD
 constexpr size_t kAlign = 256;
+constexpr size_t kMaxDynamicLds = 65536;  // dynamic LDS a decode workgroup may use
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool is16bit(int t) { return t == PKV_F16 || t == PKV_BF16; }
@@ -102,6 +103,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
       max_context_len < 0)
     return PKV_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if ((long long)num_seqs * num_q_heads > (1LL << 30)) return PKV_ERR_SHAPE;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * 16) return PKV_ERR_SHAPE;
   if (!is16bit(q_dtype)) return PKV_ERR_DTYPE;
   if (kv_dtype != q_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
@@ -148,7 +150,25 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   a.max_blocks = max_blocks_per_seq;
   a.num_parts = plan.num_parts;
   a.part_blocks = plan.part_tokens / 16;
-  a.num_items = (int)items;
+  // Sequences per workgroup: the matrix-core kernel puts up to 16 / G neighbouring
+  // sequences (one wavefront each) in a workgroup, so that sequences sharing blocks can
+  // read them once; group mode needs the tile list to fit in LDS.
+  int per_group = 1;
+  bool group_mode = false;
+  if (group > 1) {
+    per_group = 16 / group < pkv::kMaxSeqsPerGroup ? 16 / group : pkv::kMaxSeqsPerGroup;
+    // (list entries keep the logical block index in 16 bits)
+    group_mode = per_group > 1 && (long long)per_group * a.part_blocks <= pkv::kMaxGroupListEntries &&
+                 max_blocks_per_seq <= 65536;
+    if (pkv::mfma_decode_lds_bytes(head_dim, per_group, a.part_blocks, group_mode) > kMaxDynamicLds)
+      group_mode = false;
+    if (pkv::mfma_decode_lds_bytes(head_dim, per_group, a.part_blocks, group_mode) > kMaxDynamicLds)
+      per_group = 1;
+  }
+  a.seqs_per_group = per_group;
+  a.num_seq_groups = (num_seqs + per_group - 1) / per_group;
+  a.group_mode_ok = group_mode ? 1 : 0;
+  a.num_items = (int)((long long)a.num_seq_groups * num_kv_heads * plan.num_parts);
   const float log2e = 1.4426950408889634f;
   const bool fp8 = kv_dtype == PKV_FP8_E4M3;
   a.qk_scale_log2 = scale * log2e * (fp8 ? k_scale : 1.0f);

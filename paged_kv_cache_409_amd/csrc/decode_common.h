@@ -22,15 +22,18 @@ struct DecodeArgs {
   int max_blocks;                 // block-table row length
   int num_parts;                  // partitions per sequence (grid dimension)
   int part_blocks;                // KV blocks per partition
-  int num_items;                  // num_seqs * num_kv_heads * num_parts
+  int num_items;                  // workgroups with work: num_seq_groups * num_kv_heads * num_parts
+  int seqs_per_group;             // sequences (one wavefront each) per workgroup; 1 for the VALU kernel
+  int num_seq_groups;             // ceil(num_seqs / seqs_per_group)
+  int group_mode_ok;              // the workgroup's LDS holds a tile list for sharing groups
   float qk_scale_log2;            // scale * log2(e) (* k_scale for an fp8 cache)
   float v_scale;                  // 1, or v_scale for an fp8 cache
 };
 
 // Workgroup -> work item. Workgroups are dealt to the 8 XCDs round-robin; this map
-// gives each run of 4 consecutive items (the 4 beams of one request when sequences
-// are laid out request-major) to a single XCD, so blocks they share stay in that
-// XCD's L2. The grid is padded to a multiple of 32; ids past num_items do nothing.
+// gives each run of 4 consecutive items (neighbouring sequences, or sequence groups)
+// to a single XCD, so blocks they share stay in that XCD's L2. The grid is padded to a
+// multiple of 32; ids past num_items do nothing.
 __device__ __forceinline__ int item_of_workgroup(int w) {
   const int xcd = w & 7, k = w >> 3;
   return (((k >> 2) << 3) + xcd) * 4 + (k & 3);
@@ -40,14 +43,25 @@ struct Item {
   int s, g, p;
 };
 
-// Items are ordered (kv head, partition, sequence) with the sequence fastest.
+// Items are ordered (kv head, partition, sequence group) with the group fastest; it.s is
+// the group's first sequence (groups of one sequence for the VALU kernel).
 __device__ __forceinline__ Item decode_item(int j, const DecodeArgs& a) {
   Item it;
-  it.s = j % a.num_seqs;
-  const int r = j / a.num_seqs;
+  it.s = (j % a.num_seq_groups) * a.seqs_per_group;
+  const int r = j / a.num_seq_groups;
   it.p = r % a.num_parts;
   it.g = r / a.num_parts;
   return it;
+}
+
+// Orders a wavefront's own LDS writes before its later LDS reads of other lanes' data
+// (what a workgroup barrier does for a one-wave workgroup), without involving the
+// other wavefronts of the workgroup.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

@@ -4,26 +4,33 @@
 // Softmax(Q K^T / sqrt(d)) V; only the read of K and V changes, which are gathered
 // through the sequence's block table from 16-token physical blocks
 // ("vLLM 推理优化技术深度调研报告", 维度一.1 误解二 and 维度一.3 公式 3-4;
-// "vLLM推理引擎PagedAttention原理与性能优化实战", §2.2).
+// "vLLM推理引擎PagedAttention原理与性能优化实战", §2.2). Sequences forked from one prompt
+// (beams) share its blocks ("vLLM推理引擎PagedAttention原理与性能优化实战", §3.1-3.2).
 //
 // How it is computed here (this design is not from the pages):
-// * one wavefront per (sequence, kv head, context partition);
-// * the partition's block-table slice is staged in LDS;
-// * per 16-token block the G query heads of the kv head form a small dense
-//   contraction: S^T[16 tok x 16 heads] = K[16 x D] . Q^T[D x 16] on
-//   v_mfma_f32_16x16x32 (heads padded to 16 columns), then
-//   O^T[D x 16 heads] += V^T[D x 16 tok] . P[16 tok x 16 heads] on
-//   v_mfma_f32_16x16x16. The accumulator layout of S^T is exactly the operand
-//   layout P needs, so softmax weights never leave their lanes;
-// * K goes straight from HBM into MFMA operand registers (16-byte buffer loads);
-//   V is staged through LDS (XOR-swizzled 16-byte chunks) and read back transposed
-//   with ds_read_b64_tr_b16;
-// * online softmax in fp32 with exp2 (log2 e folded into the scale); the running
-//   max is combined across the four lane rows with permlane16/32 swaps;
-// * tokens past the partition's end are excluded by select (K side) and by zeroing their
-//   V rows (0 * stale NaN would otherwise poison the product);
-// * an fp8 (OCP E4M3FN) cache is widened exactly to the q dtype in registers; its
-//   per-tensor scales are folded into the logit scale and the output scale.
+// * a workgroup holds B = 16 / G wavefronts for B consecutive sequences of one kv head
+//   and one context partition;
+// * per 16-token block the query heads form a small dense contraction:
+//   S^T[16 tok x 16 cols] = K[16 x D] . Q^T[D x 16] on v_mfma_f32_16x16x32, then
+//   O^T[D x 16 cols] += V^T[D x 16 tok] . P[16 tok x 16 cols] on v_mfma_f32_16x16x16.
+//   The accumulator layout of S^T is exactly the operand layout P needs, so softmax
+//   weights never leave their lanes;
+// * independent mode: each wavefront runs its own sequence; its G query heads are
+//   columns 0..G-1 (the rest are masked);
+// * group mode, when the workgroup's sequences share blocks: the 16 columns are the
+//   B sequences x G heads. Wave 0 lists, per logical block, the distinct physical
+//   blocks of the B sequences with the set of sequences that read each; the waves split
+//   that list, so a shared block is read from HBM and multiplied once for all of its
+//   readers; at the end the waves' softmax states are merged in LDS;
+// * V (and K for blocks read once) is loaded with whole rows per instruction, staged in
+//   LDS as XOR-swizzled 16-byte chunks and read back as MFMA operands (V transposed with
+//   ds_read_b64_tr_b16);
+// * online softmax in fp32 with exp2 (log2 e folded into the scale); the running max
+//   of a column is combined across its four lane rows with permlane16/32 swaps;
+// * tokens outside a column's context are excluded by select, and V rows past every
+//   reader's context are zeroed (0 * stale NaN would otherwise poison the product);
+// * an fp8 (OCP E4M3FN) cache is widened exactly to the q dtype; its per-tensor scales
+//   are folded into the logit scale and the output scale.
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -37,7 +44,7 @@ struct MfmaTraits {
   static constexpr int kLoads = kTileBytes / (16 * kWave);  // 16-byte loads per lane per tile
   static constexpr int kRowChunks = D / 8;              // 16-byte chunks per 16-bit row in LDS
   static constexpr int kTileLds = kBlock * D * 2;       // one tile in LDS, 16-bit elements
-  static constexpr int kLdsBytes = 2 * kTileLds;        // K tile, then V tile
+  static constexpr int kLdsBytes = 2 * kTileLds;        // K tile, then V tile (per wavefront)
 };
 
 template <int QT>
@@ -84,35 +91,32 @@ template <int QT, int KVT, int D>
 struct Tile {
   u32x4 k[MfmaTraits<QT, KVT, D>::kLoads];
   u32x4 v[MfmaTraits<QT, KVT, D>::kLoads];
+  int pos;          // logical block index within the sequences
+  int rows;         // V rows [0, rows) hold live tokens of some reader; the rest are zeroed
+  uint32_t readers; // bit b: sequence b of the group reads this block (bit 0 in independent mode)
 };
 
-// One work item: the G query heads of kv head it.g of sequence it.s over context
-// partition it.p, which holds tokens [start, ctx) up to the partition's end.
-template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO, bool KLDS>
-__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, const int ctx, const int start,
-                                          int* bt_lds, uint8_t (*kv_lds)[MfmaTraits<QT, KVT, D>::kLdsBytes]) {
+// Running softmax state of one wavefront: per lane (column n, rows 4*j4..4*j4+3 of each
+// 16-row chunk of D).
+template <int D>
+struct State {
+  f32x4 o[D / 16];
+  float m, l;
+};
+
+// The tiles of one wavefront. With LIST, tile k is entry k * stride of (ids, meta); meta
+// packs the logical block index (bits 0-15), the reader set (bits 16-23) and the live V
+// rows (bits 24-28). Without LIST, ids is the block-table slice and tile k is logical
+// block pos0 + k, read by sequence 0, with live rows up to `tile_end`.
+// col_bit / col_end: the reader bit of this lane's column (0: padded column), and the end
+// (exclusive, absolute token index) of that reader's context in this partition.
+template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO, bool KLDS, bool LIST>
+__device__ __forceinline__ void mfma_tiles(const DecodeArgs& a, const int g, const int ntiles, const int* ids,
+                                           const int* meta, const int stride, const int pos0, const int tile_end,
+                                           const u32x4* qb, const uint32_t col_bit, const int col_end,
+                                           uint8_t* lds, State<D>& st) {
   using Tr = MfmaTraits<QT, KVT, D>;
-  const int lane = threadIdx.x, n = lane & 15, j4 = lane >> 4;
-  const int G = a.group;
-  const int head = it.g * G + n;
-  const int end = min(ctx, start + a.part_blocks * kBlock);
-  const int nblk = (end - start + kBlock - 1) / kBlock;
-
-  // Stage this partition's block-table slice in LDS.
-  {
-    const int32_t* bt = a.block_tables + (int64_t)it.s * a.max_blocks + (start / kBlock);
-    for (int i = lane; i < nblk; i += kWave) bt_lds[i] = bt[i];
-  }
-
-  // Q^T as the B operand of the QK steps (rows of padded heads are zero).
-  u32x4 qb[Tr::kQk];
-  {
-    const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)it.s * a.q_seq_stride + (int64_t)head * D;
-#pragma unroll
-    for (int c = 0; c < Tr::kQk; ++c)
-      qb[c] = (n < G) ? *(const u32x4*)(qrow + qk_d0<KVT>(c, j4)) : u32x4{0u, 0u, 0u, 0u};
-  }
-  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1), n = lane & 15, j4 = lane >> 4;
 
   // Per-lane byte offsets inside one kv head's tile. V (and K through LDS): lane l reads
   // bytes [16 (64 u + l), +16) with load u, one contiguous KiB per instruction. K straight
@@ -126,16 +130,34 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, co
     else if constexpr (KVT == kFP8)
       koff[u] = n * D + 64 * u + 16 * j4;                       // row n, 16 fp8 values
     else
-      koff[u] = (n * D + qk_d0<KVT>(u, j4)) * 2;          // row n, 8 values
+      koff[u] = (n * D + qk_d0<KVT>(u, j4)) * 2;                // row n, 8 values
   }
 
   const int64_t head_stride = (int64_t)Tr::kTileBytes;
-  const uint8_t* kbase = (const uint8_t*)a.k_cache + (int64_t)it.g * head_stride;
-  const uint8_t* vbase = (const uint8_t*)a.v_cache + (int64_t)it.g * head_stride;
+  const uint8_t* kbase = (const uint8_t*)a.k_cache + (int64_t)g * head_stride;
+  const uint8_t* vbase = (const uint8_t*)a.v_cache + (int64_t)g * head_stride;
   const int64_t block_stride = (int64_t)a.num_kv_heads * head_stride;
 
-  auto load = [&](Tile<QT, KVT, D>& t, int i) {
-    const int id = readfirstlane(i < nblk ? bt_lds[i < nblk ? i : 0] : -1);
+  auto load = [&](Tile<QT, KVT, D>& t, int k) {
+    int id = -1, pos = 0, rows = 0, readers = 0;
+    if (k < ntiles) {
+      if constexpr (LIST) {
+        id = ids[k * stride];
+        const int m = meta[k * stride];
+        pos = m & 0xffff;
+        readers = (m >> 16) & 0xff;
+        rows = (m >> 24) & 0x1f;
+      } else {
+        id = ids[k];
+        pos = pos0 + k;
+        readers = 1;
+        rows = min(tile_end - pos * kBlock, kBlock);
+      }
+    }
+    id = readfirstlane(id);
+    t.pos = readfirstlane(pos);
+    t.rows = readfirstlane(rows);
+    t.readers = (uint32_t)readfirstlane(readers);
     const bool live = id >= 0 && id < a.num_blocks;
     const int phys = live ? id : 0;
     const uint32_t bytes = live ? (uint32_t)Tr::kTileBytes : 0u;   // 0: loads return zeros
@@ -146,12 +168,6 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, co
 #pragma unroll
     for (int u = 0; u < Tr::kLoads; ++u) t.v[u] = buf_load16<POLICY>(rv, voff[u]);
   };
-
-  f32x4 o[Tr::kPv];
-#pragma unroll
-  for (int c = 0; c < Tr::kPv; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float qk_scale = a.qk_scale_log2;
 
   // A tile -> LDS as 16-bit rows; chunk k of row r is stored at k ^ (r mod chunks). Rows
   // at or past `valid_rows` are stored as zeros when `mask` is set.
@@ -177,15 +193,16 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, co
     }
   };
 
-  auto process = [&](const Tile<QT, KVT, D>& t, int i, uint8_t* lds) {
-    uint8_t* kl = lds;
-    uint8_t* vl = lds + Tr::kTileLds;
-    // K rows past the partition are not masked here: their scores are replaced by -inf.
-    // V rows past it are zeroed, since 0 * stale NaN would poison the product.
-    const int valid_rows = end - start - i * kBlock;
+  const float qk_scale = a.qk_scale_log2;
+  uint8_t* kl = lds;
+  uint8_t* vl = lds + Tr::kTileLds;
+
+  auto process = [&](const Tile<QT, KVT, D>& t) {
+    // K rows of dead tokens are not masked here: their scores are replaced by -inf.
+    // V rows past every reader's context are zeroed.
     if constexpr (KLDS) stage(t.k, kl, false, 0);
-    stage(t.v, vl, valid_rows < kBlock, valid_rows);
-    __syncthreads();
+    stage(t.v, vl, t.rows < kBlock, t.rows);
+    wave_lds_sync();
 
     // S^T = K . Q^T for this block.
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -205,24 +222,28 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, co
       }
       sacc = mfma_qk<QT>(ka, qb[c], sacc);
     }
-    // Scores of tokens 4*j4 .. 4*j4+3 of the block for head n; masked ones are -inf.
-    const int tok0 = start + i * kBlock + 4 * j4;
+    // Scores of tokens 4*j4 .. 4*j4+3 of the block for column n; dead ones are -inf.
+    const int tok0 = t.pos * kBlock + 4 * j4;
+    const bool reads = (t.readers & col_bit) != 0u;
     float sc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < end) ? sacc[r] * qk_scale : -INFINITY;
+    for (int r = 0; r < 4; ++r) sc[r] = (reads && tok0 + r < col_end) ? sacc[r] * qk_scale : -INFINITY;
     float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mb = max_xor16(mb);
     mb = max_xor32(mb);
-    const float m_new = fmaxf(m_run, mb);
-    const float alpha = exp2_fast(m_run - m_new);
-    m_run = m_new;
-    const uint32_t p01 = pack2<QT>(exp2_fast(sc[0] - m_new), exp2_fast(sc[1] - m_new));
-    const uint32_t p23 = pack2<QT>(exp2_fast(sc[2] - m_new), exp2_fast(sc[3] - m_new));
+    const float m_new = fmaxf(st.m, mb);
+    // A column that has seen no live token yet keeps m = -inf; exponents are then taken
+    // against 0 so that they come out as exp2(-inf) = 0, never as exp2(-inf + inf).
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = st.m == m_new ? 1.0f : exp2_fast(st.m - m_ref);
+    st.m = m_new;
+    const uint32_t p01 = pack2<QT>(exp2_fast(sc[0] - m_ref), exp2_fast(sc[1] - m_ref));
+    const uint32_t p23 = pack2<QT>(exp2_fast(sc[2] - m_ref), exp2_fast(sc[3] - m_ref));
     // The denominator sums the rounded weights that the PV product uses.
-    l_run = l_run * alpha + ((lo16<QT>(p01) + hi16<QT>(p01)) + (lo16<QT>(p23) + hi16<QT>(p23)));
+    st.l = st.l * alpha + ((lo16<QT>(p01) + hi16<QT>(p01)) + (lo16<QT>(p23) + hi16<QT>(p23)));
     if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int c = 0; c < Tr::kPv; ++c) o[c] *= alpha;
+      for (int c = 0; c < Tr::kPv; ++c) st.o[c] *= alpha;
     }
 
     // O^T += V^T . P
@@ -235,85 +256,288 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const Item it, co
       const uint32_t addr = (rr * Tr::kRowChunks + (ch ^ sw)) * 16 + (n & 1) * 8;
       const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(vl + addr));
-      o[c] = mfma_pv<QT>(va, pb, o[c]);
+      st.o[c] = mfma_pv<QT>(va, pb, st.o[c]);
     }
   };
 
   // NBUF tiles in flight, kept in a ring of register tiles. The loop body has no branch
-  // around a load, so the waitcnt counts stay exact; when nblk is not a multiple of NBUF
-  // the last round processes blocks past the end, which is harmless: their loads return
-  // zeros and every one of their tokens is masked (alpha = 1, p = 0).
+  // around a load, so the waitcnt counts stay exact; when ntiles is not a multiple of
+  // NBUF the last round processes tiles past the end, which is harmless: their loads
+  // return zeros and no column reads them (alpha = 1, p = 0).
   Tile<QT, KVT, D> t[NBUF];
 #pragma unroll
   for (int b = 0; b < NBUF; ++b) load(t[b], b);
-  for (int i = 0; i < nblk; i += NBUF) {
-    if constexpr (PRIO) progress_priority(i, nblk);
+  for (int k = 0; k < ntiles; k += NBUF) {
+    if constexpr (PRIO) progress_priority(k, ntiles);
 #pragma unroll
     for (int b = 0; b < NBUF; ++b) {
-      process(t[b], i + b, kv_lds[b & 1]);
-      load(t[b], i + b + NBUF);
+      process(t[b]);
+      load(t[b], k + b + NBUF);
     }
   }
+}
 
-  const float l_tot = sum_xor32(sum_xor16(l_run));
-  if (n >= G) return;
-  const int64_t row = (int64_t)it.s * a.num_q_heads + head;
+// Q^T as the B operand of the QK steps for column n = lane & 15: query head `head` of
+// sequence s, or zeros for a padded column.
+template <int QT, int KVT, int D>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, bool valid, int s, int head, u32x4* qb) {
+  const int j4 = (threadIdx.x & (kWave - 1)) >> 4;
+  const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)s * a.q_seq_stride + (int64_t)head * D;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+    qb[c] = valid ? *(const u32x4*)(qrow + qk_d0<KVT>(c, j4)) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Column n's result: out[s, head] (one partition) or the fp32 partial of partition p.
+// `l` is the column's full sum; o holds this lane's rows.
+template <int QT, int D>
+__device__ __forceinline__ void write_column(const DecodeArgs& a, int s, int head, int p, const f32x4* o,
+                                             float m, float l) {
+  const int j4 = (threadIdx.x & (kWave - 1)) >> 4;
+  const int64_t row = (int64_t)s * a.num_q_heads + head;
   if (a.num_parts == 1) {
-    const float inv = a.v_scale / l_tot;
+    const float inv = a.v_scale / l;
     uint16_t* orow = (uint16_t*)a.out + row * D;
 #pragma unroll
-    for (int c = 0; c < Tr::kPv; ++c) {
+    for (int c = 0; c < D / 16; ++c) {
       const f32x4 v = o[c] * inv;
       *(u32x2*)(orow + 16 * c + 4 * j4) = u32x2{pack2<QT>(v[0], v[1]), pack2<QT>(v[2], v[3])};
     }
   } else {
-    const int64_t prow = row * a.num_parts + it.p;
+    const int64_t prow = row * a.num_parts + p;
     float* po = a.part_o + prow * D;
 #pragma unroll
-    for (int c = 0; c < Tr::kPv; ++c) *(f32x4*)(po + 16 * c + 4 * j4) = o[c];
-    if (j4 == 0) *(f32x2*)(a.part_ml + prow * 2) = f32x2{m_run, l_tot};
+    for (int c = 0; c < D / 16; ++c) *(f32x4*)(po + 16 * c + 4 * j4) = o[c];
+    if (j4 == 0) *(f32x2*)(a.part_ml + prow * 2) = f32x2{m, l};
   }
 }
 
+// Independent mode: one wavefront, the G query heads of kv head g of sequence s over
+// partition p, which holds tokens [start, ctx) up to the partition's end.
+template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO, bool KLDS>
+__device__ __forceinline__ void mfma_single(const DecodeArgs& a, const int s, const int g, const int p,
+                                            const int ctx, const int start, int* bt_lds, uint8_t* lds) {
+  const int lane = threadIdx.x & (kWave - 1), n = lane & 15;
+  const int G = a.group;
+  const int end = min(ctx, start + a.part_blocks * kBlock);
+  const int nblk = (end - start + kBlock - 1) / kBlock;
+  {
+    const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + (start / kBlock);
+    for (int i = lane; i < nblk; i += kWave) bt_lds[i] = bt[i];
+  }
+  u32x4 qb[D / 32];
+  load_q<QT, KVT, D>(a, n < G, s, g * G + n, qb);
+  wave_lds_sync();
+
+  State<D> st;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  mfma_tiles<QT, KVT, D, NBUF, POLICY, PRIO, KLDS, false>(a, g, nblk, bt_lds, nullptr, 1, start / kBlock, end,
+                                                          qb, n < G ? 1u : 0u, end, lds, st);
+  const float l_tot = sum_xor32(sum_xor16(st.l));
+  if (n < G) write_column<QT, D>(a, s, g * G + n, p, st.o, st.m, l_tot);
+}
+
+// Group mode: the B wavefronts of the workgroup compute sequences s0 .. s0+B-1 of kv head
+// g over partition p together. Every one of them has tokens in the partition.
 template <int QT, int KVT, int D>
-__global__ __launch_bounds__(64) void paged_decode_mfma(DecodeArgs a) {
+__device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, const int g, const int p,
+                                           const int start, uint8_t* smem) {
   using Tr = MfmaTraits<QT, KVT, D>;
-  extern __shared__ int bt_lds[];
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2][Tr::kLdsBytes];
+  const int B = a.seqs_per_group, G = a.group, PB = a.part_blocks;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1), n = lane & 15, j4 = lane >> 4;
+  uint8_t* tiles = smem;
+  int* bts = (int*)(smem + B * Tr::kLdsBytes);              // B slices of PB block ids
+  int* small = bts + B * PB;                                 // kDecodeSmallLds bytes
+  int* ends = small;                                         // [kMaxSeqsPerGroup]
+  int* count = small + kMaxSeqsPerGroup;
+  float* merge_ml = (float*)(small + 16);                    // [B][16][2]
+  int* list_id = small + kDecodeSmallLds / 4;                // up to B * PB entries
+  int* list_meta = list_id + B * PB;
+
+  // 1. Each wave stages its sequence's block-table slice and context end.
+  const int s = s0 + w;
+  const int ctx = min(a.context_lens[s], a.max_blocks * kBlock);
+  const int end = min(ctx, start + PB * kBlock);
+  const int nblk = (end - start + kBlock - 1) / kBlock;
+  {
+    const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + (start / kBlock);
+    for (int i = lane; i < nblk; i += kWave) bts[w * PB + i] = bt[i];
+  }
+  if (lane == 0) ends[w] = end;
+  __syncthreads();
+
+  // 2. Wave 0 lists the distinct physical blocks of each logical block, in logical order,
+  //    each with the set of sequences that read it.
+  if (w == 0) {
+    int npos = 0;
+    for (int b = 0; b < B; ++b) npos = max(npos, (ends[b] - start + kBlock - 1) / kBlock);
+    int base = 0;
+    for (int i0 = 0; i0 < npos; i0 += kWave) {
+      const int i = i0 + lane;
+      const int pos = start / kBlock + i;
+      int ids_b[kMaxSeqsPerGroup];
+      uint32_t live = 0;
+#pragma unroll
+      for (int b = 0; b < kMaxSeqsPerGroup; ++b) {
+        const bool has = b < B && i < npos && pos * kBlock < ends[b];
+        ids_b[b] = has ? bts[b * PB + i] : -1;
+        live |= has ? (1u << b) : 0u;
+      }
+      int cnt = 0;
+      uint32_t done = 0;
+      int e_id[kMaxSeqsPerGroup];
+      uint32_t e_readers[kMaxSeqsPerGroup];
+#pragma unroll
+      for (int b = 0; b < kMaxSeqsPerGroup; ++b) {
+        e_id[b] = -1;
+        e_readers[b] = 0;
+        if (((live >> b) & 1u) && !((done >> b) & 1u)) {
+          uint32_t rd = 0;
+#pragma unroll
+          for (int c = 0; c < kMaxSeqsPerGroup; ++c)
+            if (c >= b && ((live >> c) & 1u) && ids_b[c] == ids_b[b]) rd |= 1u << c;
+          done |= rd;
+          e_id[b] = ids_b[b];
+          e_readers[b] = rd;
+          ++cnt;
+        }
+      }
+      // Exclusive prefix sum of cnt over the lanes.
+      int before = 0, total = 0;
+      for (int k = 0; k < B; ++k) {
+        const uint64_t bal = __ballot(cnt > k);
+        before += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        total += __popcll(bal);
+      }
+      int e = base + before;
+#pragma unroll
+      for (int b = 0; b < kMaxSeqsPerGroup; ++b) {
+        if (e_readers[b] == 0u) continue;
+        int rows = 0;
+        for (int c = 0; c < B; ++c)
+          if ((e_readers[b] >> c) & 1u) rows = max(rows, min(ends[c] - pos * kBlock, kBlock));
+        list_id[e] = e_id[b];
+        list_meta[e] = pos | (int)(e_readers[b] << 16) | (rows << 24);
+        ++e;
+      }
+      base += total;
+    }
+    if (lane == 0) *count = base;
+  }
+  __syncthreads();
+
+  // 3. Every wave takes entries w, w + B, ... for all of the group's columns.
+  const int ncols = B * G;
+  const bool col_ok = n < ncols;
+  const int cb = col_ok ? n / G : 0;                         // reader (sequence) of column n
+  u32x4 qb[D / 32];
+  load_q<QT, KVT, D>(a, col_ok, s0 + cb, g * G + (col_ok ? n % G : 0), qb);
+  const int total = *count;
+  const int ntiles = total > w ? (total - w + B - 1) / B : 0;
+  State<D> st;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  mfma_tiles<QT, KVT, D, 2, kPolicyStream, true, true, true>(a, g, ntiles, list_id + w, list_meta + w, B, 0, 0, qb,
+                                                             col_ok ? (1u << cb) : 0u, col_ok ? ends[cb] : 0,
+                                                             tiles + w * Tr::kLdsBytes, st);
+  const float l_w = sum_xor32(sum_xor16(st.l));
+
+  // 4. Merge the waves' states column by column (the tile staging area is free again).
+  __syncthreads();
+  f32x4* merge_o = (f32x4*)tiles;                            // [B][64 lanes][kPv]
+#pragma unroll
+  for (int c = 0; c < Tr::kPv; ++c) merge_o[(w * kWave + lane) * Tr::kPv + c] = st.o[c];
+  if (j4 == 0) {
+    merge_ml[(w * 16 + n) * 2] = st.m;
+    merge_ml[(w * 16 + n) * 2 + 1] = l_w;
+  }
+  __syncthreads();
+  if (w != 0 || !col_ok) return;
+  float M = -INFINITY;
+  for (int v = 0; v < B; ++v) M = fmaxf(M, merge_ml[(v * 16 + n) * 2]);
+  float L = 0.f;
+  f32x4 o[Tr::kPv];
+#pragma unroll
+  for (int c = 0; c < Tr::kPv; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int v = 0; v < B; ++v) {
+    const float f = exp2_fast(merge_ml[(v * 16 + n) * 2] - M);   // a wave that saw no token: f = 0
+    L = fmaf(f, merge_ml[(v * 16 + n) * 2 + 1], L);
+#pragma unroll
+    for (int c = 0; c < Tr::kPv; ++c) o[c] += f * merge_o[(v * kWave + lane) * Tr::kPv + c];
+  }
+  write_column<QT, D>(a, s0 + cb, g * G + n % G, p, o, M, L);
+}
+
+template <int QT, int KVT, int D>
+__global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma(DecodeArgs a) {
+  using Tr = MfmaTraits<QT, KVT, D>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int j = item_of_workgroup(blockIdx.x);
   if (j >= a.num_items) return;
   const Item it = decode_item(j, a);
-  const int ctx = min(a.context_lens[it.s], a.max_blocks * kBlock);
+  const int B = a.seqs_per_group;
+  const int w = threadIdx.x / kWave;
   const int start = it.p * a.part_blocks * kBlock;
+
+  // Group mode when every sequence of the group has tokens in this partition and another
+  // sequence reads the first sequence's first block of it. Every wave evaluates the same
+  // condition, so the whole workgroup takes the same branch.
+  if (a.group_mode_ok && it.s + B <= a.num_seqs) {
+    const int i0 = start / kBlock;
+    const int first = a.block_tables[(int64_t)it.s * a.max_blocks + i0];
+    bool all_live = true, shares = false;
+    for (int b = 0; b < B; ++b) {
+      const int c = min(a.context_lens[it.s + b], a.max_blocks * kBlock);
+      all_live = all_live && c > start;
+      if (b > 0) shares = shares || a.block_tables[(int64_t)(it.s + b) * a.max_blocks + i0] == first;
+    }
+    if (all_live && shares) {
+      mfma_group<QT, KVT, D>(a, it.s, it.g, it.p, start, smem);
+      return;
+    }
+  }
+
+  // Independent mode: wave w runs sequence it.s + w with its own LDS areas.
+  const int s = it.s + w;
+  if (s >= a.num_seqs) return;
+  const int ctx = min(a.context_lens[s], a.max_blocks * kBlock);
   if (ctx <= start) {
     // Nothing in this partition. A whole sequence with no context writes zeros.
-    const int n = threadIdx.x & 15, j4 = threadIdx.x >> 4;
+    const int n = threadIdx.x & 15, j4 = (threadIdx.x & (kWave - 1)) >> 4;
     if (a.num_parts == 1 && n < a.group) {
-      uint16_t* o = (uint16_t*)a.out + ((int64_t)it.s * a.num_q_heads + it.g * a.group + n) * D;
+      uint16_t* o = (uint16_t*)a.out + ((int64_t)s * a.num_q_heads + it.g * a.group + n) * D;
 #pragma unroll
       for (int c = 0; c < Tr::kPv; ++c) *(u32x2*)(o + 16 * c + 4 * j4) = u32x2{0u, 0u};
     }
     return;
   }
+  uint8_t* lds = smem + w * Tr::kLdsBytes;
+  int* bt_lds = (int*)(smem + B * Tr::kLdsBytes) + w * a.part_blocks;
   // Blocks shared with a neighbouring sequence: cached loads (the other readers hit L2),
   // two tiles in flight, default priority, K straight into registers (these items are
   // bound by per-block latency more than by HBM). Private blocks stream, with K through
   // LDS; a whole context in one partition does best with one tile in flight per wave, a
   // split context (more items than wave slots) with two.
-  if (neighbour_shares_block(a, it.s, start / kBlock))
-    mfma_item<QT, KVT, D, 2, kPolicyCached, false, false>(a, it, ctx, start, bt_lds, kv_lds);
+  if (neighbour_shares_block(a, s, start / kBlock))
+    mfma_single<QT, KVT, D, 2, kPolicyCached, false, false>(a, s, it.g, it.p, ctx, start, bt_lds, lds);
   else if (a.num_parts > 1)
-    mfma_item<QT, KVT, D, 2, kPolicyStream, true, true>(a, it, ctx, start, bt_lds, kv_lds);
+    mfma_single<QT, KVT, D, 2, kPolicyStream, true, true>(a, s, it.g, it.p, ctx, start, bt_lds, lds);
   else
-    mfma_item<QT, KVT, D, 1, kPolicyStream, true, true>(a, it, ctx, start, bt_lds, kv_lds);
+    mfma_single<QT, KVT, D, 1, kPolicyStream, true, true>(a, s, it.g, it.p, ctx, start, bt_lds, lds);
 }
 
 template <int QT, int KVT, int D>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int grid = (a.num_items + 31) / 32 * 32;
-  const size_t lds = (size_t)a.part_blocks * sizeof(int);
-  hipLaunchKernelGGL((paged_decode_mfma<QT, KVT, D>), dim3(grid), dim3(kWave), lds, stream, a);
+  const size_t lds = mfma_decode_lds_bytes(D, a.seqs_per_group, a.part_blocks, a.group_mode_ok != 0);
+  hipLaunchKernelGGL((paged_decode_mfma<QT, KVT, D>), dim3(grid), dim3(kWave * a.seqs_per_group), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -26,6 +26,23 @@ struct CacheWriteArgs {
   float k_scale, v_scale;
 };
 
+// Workgroups of the matrix-core decode kernel hold up to this many sequences (one
+// wavefront each).
+constexpr int kMaxSeqsPerGroup = 4;
+// Small LDS area of a group-mode workgroup: per-sequence ends, the tile-list length and
+// the per-wave (max, sum) of every column for the final merge.
+constexpr int kDecodeSmallLds = 2048;
+// Largest group-mode tile list (entries) a workgroup stages in LDS.
+constexpr int kMaxGroupListEntries = 2048;
+
+// Dynamic LDS bytes of one matrix-core decode workgroup: per-wave K/V tile staging,
+// per-wave block-table slices, and in group mode the small area and the tile list.
+inline size_t mfma_decode_lds_bytes(int head_dim, int seqs_per_group, int part_blocks, bool group_mode) {
+  const size_t tile = (size_t)2 * 16 * head_dim * 2;
+  return seqs_per_group * tile + (size_t)seqs_per_group * part_blocks * 4 +
+         (group_mode ? kDecodeSmallLds + (size_t)2 * seqs_per_group * part_blocks * 4 : 0);
+}
+
 hipError_t launch_decode_mfma(const DecodeArgs& a, int q_type, int kv_type, int head_dim, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, int q_type, int kv_type, int head_dim, hipStream_t s);
 hipError_t launch_decode_reduce(const ReduceArgs& a, int q_type, int head_dim, hipStream_t s);
