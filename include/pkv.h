@@ -7,6 +7,7 @@
  *   pkv_paged_attention_decode  one decode step of attention over a paged KV cache
  *   pkv_reshape_and_cache       write each new token's K/V row into its cache slot
  *   pkv_copy_blocks             copy-on-write copies of whole KV blocks
+ *   pkv_decode_step             cache write + attention of one decode step, one launch
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -133,6 +134,35 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
                                int64_t q_seq_stride, int partition_size,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One whole decode step in one launch: the cache write of every sequence's new token
+ * followed by attention over the paged cache that now includes it. The results (caches
+ * and out) are those of
+ *   pkv_reshape_and_cache(key, value, slot_mapping, k_cache, v_cache, num_tokens = num_seqs, ...)
+ *   pkv_paged_attention_decode(out, q, k_cache, v_cache, ...)
+ * on the same stream, bit for bit. The work item that attends over a sequence's last
+ * position writes that sequence's new token first (the pages' memory flow: a new token's
+ * KV is registered in its block, then attention reads the blocks; "vLLM 推理优化技术深度
+ * 调研报告", 维度一.2).
+ *
+ *   key/value      [num_seqs, num_kv_heads, head_dim] q_dtype: the new token of each
+ *                  sequence; token strides key_stride / value_stride elements (0 = dense)
+ *   slot_mapping   [num_seqs] int64: slot of sequence s's new token, which must be the slot
+ *                  of its logical position context_lens[s] - 1 in its own (unshared)
+ *                  blocks; a negative slot is skipped
+ *   k_cache/v_cache written (new tokens, converted as pkv_reshape_and_cache does, fp8
+ *                  with k_scale / v_scale) and read
+ * Every other argument is as for pkv_paged_attention_decode, whose checks also apply.
+ */
+int pkv_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
+                    const void* key, const void* value, const int64_t* slot_mapping,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                    int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
+                    int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
+                    int64_t q_seq_stride, int64_t key_stride, int64_t value_stride, int partition_size,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Write the K and V rows of num_tokens new tokens into their cache slots

@@ -28,6 +28,15 @@ SIGNATURES = {
         _c_int, _c_int, _c_f, _c_f, _c_f,              # q_dtype kv_dtype scale k_scale v_scale
         _c_i64, _c_int,                                # q_seq_stride partition_size
         _c_p, _c_sz, _c_p]),                           # workspace workspace_bytes stream
+    "pkv_decode_step": (_c_int, [
+        _c_p, _c_p, _c_p, _c_p,                        # out q k_cache v_cache
+        _c_p, _c_p, _c_p,                              # key value slot_mapping
+        _c_p, _c_p,                                    # block_tables context_lens
+        _c_int, _c_int, _c_int, _c_int, _c_int,        # num_seqs num_q_heads num_kv_heads head_dim block_size
+        _c_i64, _c_int, _c_int,                        # num_blocks max_blocks_per_seq max_context_len
+        _c_int, _c_int, _c_f, _c_f, _c_f,              # q_dtype kv_dtype scale k_scale v_scale
+        _c_i64, _c_i64, _c_i64, _c_int,                # q_seq_stride key_stride value_stride partition_size
+        _c_p, _c_sz, _c_p]),                           # workspace workspace_bytes stream
     "pkv_reshape_and_cache": (_c_int, [
         _c_p, _c_p, _c_p, _c_p, _c_p,                  # key value slot_mapping k_cache v_cache
         _c_int, _c_int, _c_int, _c_int, _c_i64,        # num_tokens num_kv_heads head_dim block_size num_blocks

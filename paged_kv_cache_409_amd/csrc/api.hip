@@ -92,13 +92,25 @@ size_t pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int num
   return plan.ws_bytes;
 }
 
-int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_tables, const int32_t* context_lens,
-                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                               int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
-                               int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
-                               int64_t q_seq_stride, int partition_size,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// New tokens of a fused decode step (all null for plain decoding).
+struct NewTokens {
+  const void* key;
+  const void* value;
+  const int64_t* slot_mapping;
+  int64_t key_stride, value_stride;
+};
+
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens,
+                int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
+                int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
+                int64_t q_seq_stride, int partition_size, const NewTokens* tok,
+                void* workspace, size_t workspace_bytes, void* stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       max_context_len < 0)
     return PKV_ERR_SHAPE;
@@ -116,16 +128,25 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
     return PKV_ERR_SHAPE;
   if (q_seq_stride == 0) q_seq_stride = (int64_t)num_q_heads * head_dim;
   if (q_seq_stride < (int64_t)num_q_heads * head_dim) return PKV_ERR_SHAPE;
+  const int64_t kv_row = (int64_t)num_kv_heads * head_dim;
+  int64_t key_stride = 0, value_stride = 0;
+  if (tok) {
+    key_stride = tok->key_stride ? tok->key_stride : kv_row;
+    value_stride = tok->value_stride ? tok->value_stride : kv_row;
+    if (key_stride < kv_row || value_stride < kv_row) return PKV_ERR_SHAPE;
+  }
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
+  if (tok && (!tok->key || !tok->value || !tok->slot_mapping)) return PKV_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || q_seq_stride % 8 != 0)
+    return PKV_ERR_ALIGN;
+  if (tok && (!aligned16(tok->key) || !aligned16(tok->value) || key_stride % 8 != 0 || value_stride % 8 != 0))
     return PKV_ERR_ALIGN;
 
   Plan plan;
   const int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size, &plan);
   if (st != PKV_OK) return st;
-  const long long items = (long long)num_seqs * num_kv_heads * plan.num_parts;
-  if (items > (1LL << 30)) return PKV_ERR_SHAPE;
+  if ((long long)num_seqs * num_kv_heads * plan.num_parts > (1LL << 30)) return PKV_ERR_SHAPE;
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes) return PKV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PKV_ERR_ALIGN;
@@ -173,6 +194,14 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   const bool fp8 = kv_dtype == PKV_FP8_E4M3;
   a.qk_scale_log2 = scale * log2e * (fp8 ? k_scale : 1.0f);
   a.v_scale = fp8 ? v_scale : 1.0f;
+  a.new_key = tok ? tok->key : nullptr;
+  a.new_value = tok ? tok->value : nullptr;
+  a.slot_mapping = tok ? tok->slot_mapping : nullptr;
+  a.key_stride = key_stride;
+  a.value_stride = value_stride;
+  a.num_slots = num_blocks * 16;
+  a.k_quant = fp8 ? k_scale : 1.0f;
+  a.v_quant = fp8 ? v_scale : 1.0f;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int qt = q_dtype == PKV_BF16 ? pkv::kBF16 : pkv::kF16;
@@ -195,6 +224,36 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
     e = pkv::launch_decode_reduce(r, qt, head_dim, s);
   }
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                               int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
+                               int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
+                               int64_t q_seq_stride, int partition_size,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, scale,
+                     k_scale, v_scale, q_seq_stride, partition_size, nullptr, workspace, workspace_bytes, stream);
+}
+
+int pkv_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
+                    const void* key, const void* value, const int64_t* slot_mapping,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                    int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
+                    int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
+                    int64_t q_seq_stride, int64_t key_stride, int64_t value_stride, int partition_size,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const NewTokens tok{key, value, slot_mapping, key_stride, value_stride};
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, scale,
+                     k_scale, v_scale, q_seq_stride, partition_size, &tok, workspace, workspace_bytes, stream);
 }
 
 int pkv_reshape_and_cache(const void* key, const void* value, const int64_t* slot_mapping,

@@ -14,24 +14,6 @@
 
 namespace pkv {
 
-// OCP E4M3FN encoder, written from the format's definition: bias 7, 3 mantissa bits,
-// no infinities, S.1111.111 = NaN, largest finite 448, smallest subnormal 2^-9.
-__device__ __forceinline__ uint32_t e4m3_from_f32(float x) {
-  const uint32_t b = __float_as_uint(x);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const float ax = fabsf(x);
-  if (ax != ax) return 0x7Fu | sign;                 // NaN
-  if (ax >= 448.0f) return 0x7Eu | sign;             // saturate (infinities too)
-  if (ax < 0.015625f) {                              // below 2^-6: multiples of 2^-9
-    return (uint32_t)__builtin_rintf(ax * 512.0f) | sign;   // exact scaling, then RNE
-  }
-  const uint32_t ab = __float_as_uint(ax);
-  const uint32_t r = ab + 0x7FFFFu + ((ab >> 20) & 1u);     // RNE at the 3rd mantissa bit
-  const uint32_t e = (r >> 23) - 127u + 7u;                   // biased E4M3 exponent, 1..15
-  return sign | (e << 3) | ((r >> 20) & 7u);
-}
-
-
 // One thread per 8 consecutive elements of one (token, kv head) row.
 template <int IT, int KVT>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a) {
@@ -47,28 +29,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
   const int64_t dst = ((blk * a.num_kv_heads + h) * kBlock + off) * a.head_dim + 8 * c;
   const u32x4 kin = *(const u32x4*)((const uint16_t*)a.key + t * a.key_stride + (int64_t)h * a.head_dim + 8 * c);
   const u32x4 vin = *(const u32x4*)((const uint16_t*)a.value + t * a.value_stride + (int64_t)h * a.head_dim + 8 * c);
-  if constexpr (KVT == kFP8) {
-    u32x2 ko, vo;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      uint32_t kk = 0, vv = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t kp = kin[2 * w + e / 2], vp = vin[2 * w + e / 2];
-        const float kx = (e & 1) ? hi16<IT>(kp) : lo16<IT>(kp);
-        const float vx = (e & 1) ? hi16<IT>(vp) : lo16<IT>(vp);
-        kk |= e4m3_from_f32(kx / a.k_scale) << (8 * e);
-        vv |= e4m3_from_f32(vx / a.v_scale) << (8 * e);
-      }
-      ko[w] = kk;
-      vo[w] = vv;
-    }
-    *(u32x2*)((uint8_t*)a.k_cache + dst) = ko;
-    *(u32x2*)((uint8_t*)a.v_cache + dst) = vo;
-  } else {
-    *(u32x4*)((uint16_t*)a.k_cache + dst) = kin;
-    *(u32x4*)((uint16_t*)a.v_cache + dst) = vin;
-  }
+  store_cache_chunk<IT, KVT>(kin, a.k_cache, dst, a.k_scale);
+  store_cache_chunk<IT, KVT>(vin, a.v_cache, dst, a.v_scale);
 }
 
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, int in_type, int kv_type, hipStream_t stream) {

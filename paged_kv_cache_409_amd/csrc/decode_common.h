@@ -28,6 +28,14 @@ struct DecodeArgs {
   int group_mode_ok;              // the workgroup's LDS holds a tile list for sharing groups
   float qk_scale_log2;            // scale * log2(e) (* k_scale for an fp8 cache)
   float v_scale;                  // 1, or v_scale for an fp8 cache
+  // Fused step only (new_key == nullptr otherwise): the new token of every sequence,
+  // written into its slot by the work item that holds the sequence's last position.
+  const void* new_key;            // [S, Hkv, D] q dtype, token stride key_stride elements
+  const void* new_value;          // [S, Hkv, D] q dtype, token stride value_stride elements
+  const int64_t* slot_mapping;    // [S]: slot of each new token; negative = no write
+  int64_t key_stride, value_stride;
+  int64_t num_slots;              // num_blocks * 16
+  float k_quant, v_quant;         // fp8 scales the new values are divided by
 };
 
 // Workgroup -> work item. Workgroups are dealt to the 8 XCDs round-robin; this map
@@ -62,6 +70,86 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Fused step: the work item of partition p of a sequence with (clamped) context length
+// ctx writes that sequence's new token when p holds position ctx - 1 (partition 0 when
+// ctx is 0).
+__device__ __forceinline__ bool owns_new_token(const DecodeArgs& a, int ctx, int p) {
+  if (a.new_key == nullptr) return false;
+  const int last = ctx > 0 ? ctx - 1 : 0;
+  return p == min(last / (a.part_blocks * kBlock), a.num_parts - 1);
+}
+
+// Fused step: one lane's share of sequence s's new token for kv head g, already in the
+// cache's storage format: lanes 0 .. D/8-1 hold 8 elements of its K row, lanes D/8 ..
+// D/4-1 8 elements of its V row. The work item keeps the row in registers and in an LDS
+// copy (stage_new_token): the tile that holds the token's position is patched from that
+// copy before use (the cache slot still holds stale bytes), and the row is stored into
+// the cache at the end of the item, where the store does not compete with the item's
+// loads. No other work item reads the slot.
+struct TokenChunk {
+  u32x4 data;    // converted chunk (fp8: 8 codes in the first two dwords)
+  int64_t dst;   // element index in the cache
+  bool store;    // this lane stores a chunk
+  bool is_v;
+  bool written;  // the token has a valid slot (the same in every lane): only then does the
+                 // item see it in place of the slot's old bytes, as after a separate write
+};
+
+template <int QT, int KVT, int D>
+__device__ __forceinline__ TokenChunk load_new_token(const DecodeArgs& a, int s, int g) {
+  constexpr int kChunks = D / 8;
+  TokenChunk t;
+  t.data = u32x4{0u, 0u, 0u, 0u};
+  t.dst = 0;
+  t.store = false;
+  t.is_v = false;
+  const int64_t slot = a.slot_mapping[s];
+  t.written = slot >= 0 && slot < a.num_slots;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (lane >= 2 * kChunks) return t;
+  // The slot and the row are loaded independently (neither address depends on the other).
+  t.is_v = lane >= kChunks;
+  const int c = t.is_v ? lane - kChunks : lane;
+  const uint16_t* src = (const uint16_t*)(t.is_v ? a.new_value : a.new_key) +
+                        (int64_t)s * (t.is_v ? a.value_stride : a.key_stride) + (int64_t)g * D + 8 * c;
+  t.data = convert_cache_chunk<QT, KVT>(*(const u32x4*)src, t.is_v ? a.v_quant : a.k_quant);
+  t.store = t.written;
+  t.dst = t.store ? ((slot / kBlock * a.num_kv_heads + g) * kBlock + slot % kBlock) * D + 8 * c : 0;
+  return t;
+}
+
+// Bytes of one cache row (one token, one kv head) in storage format.
+template <int KVT, int D>
+constexpr int row_bytes() { return D * (KVT == kFP8 ? 1 : 2); }
+
+// Writes the lane's chunk into `rows` (K row, then V row, storage format). Every lane of
+// the wavefront calls this; lanes without a chunk write nothing.
+template <int KVT, int D>
+__device__ __forceinline__ void stage_new_token(const TokenChunk& t, uint8_t* rows) {
+  constexpr int kChunks = D / 8, kChunkBytes = 8 * (KVT == kFP8 ? 1 : 2);
+  const int lane = threadIdx.x & (kWave - 1);
+  if (lane >= 2 * kChunks) return;
+  uint8_t* dst = rows + (t.is_v ? row_bytes<KVT, D>() : 0) + (lane % kChunks) * kChunkBytes;
+  if constexpr (KVT == kFP8)
+    *(u32x2*)dst = u32x2{t.data[0], t.data[1]};
+  else
+    *(u32x4*)dst = t.data;
+}
+
+template <int KVT>
+__device__ __forceinline__ void store_new_token(const DecodeArgs& a, const TokenChunk& t) {
+  if (t.store) store_converted_chunk<KVT>(t.data, const_cast<void*>(t.is_v ? a.v_cache : a.k_cache), t.dst);
+}
+
+// Replaces the bytes a lane loaded for one 16-byte piece of a tile with the new token's
+// bytes when the piece lies in the token's row: `off` is the piece's byte offset in the
+// tile (rows of row_bytes each), `row` the token's row in the block, `src` its row copy.
+template <int KVT, int D>
+__device__ __forceinline__ void patch_piece(u32x4& piece, uint32_t off, int row, const uint8_t* src) {
+  constexpr int RB = row_bytes<KVT, D>();
+  if ((int)(off / RB) == row) piece = *(const u32x4*)(src + off % RB);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

@@ -110,11 +110,17 @@ struct State {
 // block pos0 + k, read by sequence 0, with live rows up to `tile_end`.
 // col_bit / col_end: the reader bit of this lane's column (0: padded column), and the end
 // (exclusive, absolute token index) of that reader's context in this partition.
+// Fused step: the tile that holds a new token is patched with the token's row before use
+// (its cache slot still holds stale bytes). Without LIST: the token is at logical block
+// `ppos` (-1: none), row `prow`, its rows in LDS at `tok_rows`. With LIST: sequence b of
+// the group has its token at block patch_pos[b] (-1: none), row patch_row[b], rows at
+// tok_rows + b * kTokenRowsLds; only a block with a single reader can hold one.
 template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO, bool KLDS, bool LIST>
 __device__ __forceinline__ void mfma_tiles(const DecodeArgs& a, const int g, const int ntiles, const int* ids,
                                            const int* meta, const int stride, const int pos0, const int tile_end,
                                            const u32x4* qb, const uint32_t col_bit, const int col_end,
-                                           uint8_t* lds, State<D>& st) {
+                                           uint8_t* lds, State<D>& st, const int ppos, const int prow,
+                                           const int* patch_pos, const int* patch_row, const uint8_t* tok_rows) {
   using Tr = MfmaTraits<QT, KVT, D>;
   const int lane = threadIdx.x & (kWave - 1), n = lane & 15, j4 = lane >> 4;
 
@@ -197,7 +203,29 @@ __device__ __forceinline__ void mfma_tiles(const DecodeArgs& a, const int g, con
   uint8_t* kl = lds;
   uint8_t* vl = lds + Tr::kTileLds;
 
-  auto process = [&](const Tile<QT, KVT, D>& t) {
+  auto process = [&](Tile<QT, KVT, D>& t) {
+    // Fused step: swap the new token's row into the tile.
+    int trow = -1;
+    const uint8_t* tsrc = tok_rows;
+    if constexpr (LIST) {
+      const uint32_t r = t.readers;
+      if (r != 0u && (r & (r - 1u)) == 0u) {
+        const int b = __builtin_ctz(r);
+        if (patch_pos[b] == t.pos) {
+          trow = patch_row[b];
+          tsrc = tok_rows + b * kTokenRowsLds;
+        }
+      }
+    } else {
+      if (t.pos == ppos) trow = prow;
+    }
+    if (trow >= 0) {
+#pragma unroll
+      for (int u = 0; u < Tr::kLoads; ++u) {
+        patch_piece<KVT, D>(t.k[u], koff[u], trow, tsrc);
+        patch_piece<KVT, D>(t.v[u], voff[u], trow, tsrc + row_bytes<KVT, D>());
+      }
+    }
     // K rows of dead tokens are not masked here: their scores are replaced by -inf.
     // V rows past every reader's context are zeroed.
     if constexpr (KLDS) stage(t.k, kl, false, 0);
@@ -316,7 +344,8 @@ __device__ __forceinline__ void write_column(const DecodeArgs& a, int s, int hea
 // partition p, which holds tokens [start, ctx) up to the partition's end.
 template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO, bool KLDS>
 __device__ __forceinline__ void mfma_single(const DecodeArgs& a, const int s, const int g, const int p,
-                                            const int ctx, const int start, int* bt_lds, uint8_t* lds) {
+                                            const int ctx, const int start, int* bt_lds, uint8_t* lds,
+                                            uint8_t* tok_rows, const bool writes, const TokenChunk& token) {
   const int lane = threadIdx.x & (kWave - 1), n = lane & 15;
   const int G = a.group;
   const int end = min(ctx, start + a.part_blocks * kBlock);
@@ -325,6 +354,7 @@ __device__ __forceinline__ void mfma_single(const DecodeArgs& a, const int s, co
     const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + (start / kBlock);
     for (int i = lane; i < nblk; i += kWave) bt_lds[i] = bt[i];
   }
+  if (writes) stage_new_token<KVT, D>(token, tok_rows);
   u32x4 qb[D / 32];
   load_q<QT, KVT, D>(a, n < G, s, g * G + n, qb);
   wave_lds_sync();
@@ -334,8 +364,13 @@ __device__ __forceinline__ void mfma_single(const DecodeArgs& a, const int s, co
   for (int c = 0; c < D / 16; ++c) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
+  // The new token sits at the sequence's last position, ctx - 1.
   mfma_tiles<QT, KVT, D, NBUF, POLICY, PRIO, KLDS, false>(a, g, nblk, bt_lds, nullptr, 1, start / kBlock, end,
-                                                          qb, n < G ? 1u : 0u, end, lds, st);
+                                                          qb, n < G ? 1u : 0u, end, lds, st,
+                                                          writes && token.written ? (ctx - 1) / kBlock : -1,
+                                                          (ctx - 1) % kBlock,
+                                                          nullptr, nullptr, tok_rows);
+  if (writes) store_new_token<KVT>(a, token);
   const float l_tot = sum_xor32(sum_xor16(st.l));
   if (n < G) write_column<QT, D>(a, s, g * G + n, p, st.o, st.m, l_tot);
 }
@@ -349,24 +384,36 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
   const int B = a.seqs_per_group, G = a.group, PB = a.part_blocks;
   const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1), n = lane & 15, j4 = lane >> 4;
   uint8_t* tiles = smem;
-  int* bts = (int*)(smem + B * Tr::kLdsBytes);              // B slices of PB block ids
+  uint8_t* tok_rows = smem + B * Tr::kLdsBytes;             // B new-token row copies
+  int* bts = (int*)(tok_rows + B * kTokenRowsLds);           // B slices of PB block ids
   int* small = bts + B * PB;                                 // kDecodeSmallLds bytes
   int* ends = small;                                         // [kMaxSeqsPerGroup]
   int* count = small + kMaxSeqsPerGroup;
   float* merge_ml = (float*)(small + 16);                    // [B][16][2]
+  int* patch_pos = small + 160;                              // [B] new token's block, -1: none
+  int* patch_row = small + 168;                              // [B] its row in the block
   int* list_id = small + kDecodeSmallLds / 4;                // up to B * PB entries
   int* list_meta = list_id + B * PB;
 
-  // 1. Each wave stages its sequence's block-table slice and context end.
+  // 1. Each wave stages its sequence's block-table slice and context end, and writes its
+  //    sequence's new token (fused step).
   const int s = s0 + w;
   const int ctx = min(a.context_lens[s], a.max_blocks * kBlock);
+  const bool writes = owns_new_token(a, ctx, p);
+  TokenChunk token = {};
+  if (writes) token = load_new_token<QT, KVT, D>(a, s, g);
   const int end = min(ctx, start + PB * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
   {
     const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + (start / kBlock);
     for (int i = lane; i < nblk; i += kWave) bts[w * PB + i] = bt[i];
   }
-  if (lane == 0) ends[w] = end;
+  if (lane == 0) {
+    ends[w] = end;
+    patch_pos[w] = writes && token.written ? (ctx - 1) / kBlock : -1;
+    patch_row[w] = (ctx - 1) % kBlock;
+  }
+  if (writes) stage_new_token<KVT, D>(token, tok_rows + w * kTokenRowsLds);
   __syncthreads();
 
   // 2. Wave 0 lists the distinct physical blocks of each logical block, in logical order,
@@ -445,7 +492,9 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
   st.l = 0.f;
   mfma_tiles<QT, KVT, D, 2, kPolicyStream, true, true, true>(a, g, ntiles, list_id + w, list_meta + w, B, 0, 0, qb,
                                                              col_ok ? (1u << cb) : 0u, col_ok ? ends[cb] : 0,
-                                                             tiles + w * Tr::kLdsBytes, st);
+                                                             tiles + w * Tr::kLdsBytes, st, -1, 0,
+                                                             patch_pos, patch_row, tok_rows);
+  if (writes) store_new_token<KVT>(a, token);
   const float l_w = sum_xor32(sum_xor16(st.l));
 
   // 4. Merge the waves' states column by column (the tile staging area is free again).
@@ -508,7 +557,11 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
   const int s = it.s + w;
   if (s >= a.num_seqs) return;
   const int ctx = min(a.context_lens[s], a.max_blocks * kBlock);
+  const bool writes = owns_new_token(a, ctx, it.p);
+  TokenChunk token = {};
+  if (writes) token = load_new_token<QT, KVT, D>(a, s, it.g);
   if (ctx <= start) {
+    if (writes) store_new_token<KVT>(a, token);
     // Nothing in this partition. A whole sequence with no context writes zeros.
     const int n = threadIdx.x & 15, j4 = (threadIdx.x & (kWave - 1)) >> 4;
     if (a.num_parts == 1 && n < a.group) {
@@ -519,18 +572,19 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
     return;
   }
   uint8_t* lds = smem + w * Tr::kLdsBytes;
-  int* bt_lds = (int*)(smem + B * Tr::kLdsBytes) + w * a.part_blocks;
+  uint8_t* tok_rows = smem + B * Tr::kLdsBytes + w * kTokenRowsLds;
+  int* bt_lds = (int*)(smem + B * (Tr::kLdsBytes + kTokenRowsLds)) + w * a.part_blocks;
   // Blocks shared with a neighbouring sequence: cached loads (the other readers hit L2),
   // two tiles in flight, default priority, K straight into registers (these items are
   // bound by per-block latency more than by HBM). Private blocks stream, with K through
   // LDS; a whole context in one partition does best with one tile in flight per wave, a
   // split context (more items than wave slots) with two.
   if (neighbour_shares_block(a, s, start / kBlock))
-    mfma_single<QT, KVT, D, 2, kPolicyCached, false, false>(a, s, it.g, it.p, ctx, start, bt_lds, lds);
+    mfma_single<QT, KVT, D, 2, kPolicyCached, false, false>(a, s, it.g, it.p, ctx, start, bt_lds, lds, tok_rows, writes, token);
   else if (a.num_parts > 1)
-    mfma_single<QT, KVT, D, 2, kPolicyStream, true, true>(a, s, it.g, it.p, ctx, start, bt_lds, lds);
+    mfma_single<QT, KVT, D, 2, kPolicyStream, true, true>(a, s, it.g, it.p, ctx, start, bt_lds, lds, tok_rows, writes, token);
   else
-    mfma_single<QT, KVT, D, 1, kPolicyStream, true, true>(a, s, it.g, it.p, ctx, start, bt_lds, lds);
+    mfma_single<QT, KVT, D, 1, kPolicyStream, true, true>(a, s, it.g, it.p, ctx, start, bt_lds, lds, tok_rows, writes, token);
 }
 
 template <int QT, int KVT, int D>

@@ -103,7 +103,8 @@ struct VTile {
 // holds tokens [start, ctx) up to the partition's end.
 template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO>
 __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, const int ctx, const int start,
-                                          int* bt_lds) {
+                                          int* bt_lds, uint8_t* tok_rows, const bool writes,
+                                          const TokenChunk& token) {
   using Tr = ValuTraits<QT, KVT, D>;
   constexpr int LPR = Tr::kLanesPerRow, RPL = Tr::kRowsPerLoad;
   const int lane = threadIdx.x, grp = lane / LPR, col0 = (lane % LPR) * Tr::kCols;
@@ -114,6 +115,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, co
     const int32_t* bt = a.block_tables + (int64_t)it.s * a.max_blocks + (start / kBlock);
     for (int i = lane; i < nblk; i += kWave) bt_lds[i] = bt[i];
   }
+  if (writes) stage_new_token<KVT, D>(token, tok_rows);
 
   // q columns [col0, col0 + kCols) as packed 16-bit pairs.
   uint32_t qv[Tr::kWords];
@@ -126,6 +128,10 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, co
     }
   }
   __syncthreads();
+  // Fused step: the tile of the new token (the sequence's last position, ctx - 1) gets the
+  // token's row from its LDS copy before use; the cache slot still holds stale bytes.
+  const int patch_tile = writes && token.written ? (ctx - 1) / kBlock - start / kBlock : -1;
+  const int patch_row = (ctx - 1) % kBlock;
 
   const int64_t head_stride = (int64_t)Tr::kTileBytes;
   const uint8_t* kbase = (const uint8_t*)a.k_cache + (int64_t)it.g * head_stride;
@@ -152,7 +158,14 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, co
   float m_run = -INFINITY, l_run = 0.f;
   const float qk_scale = a.qk_scale_log2;
 
-  auto process = [&](const VTile<QT, KVT, D>& t, int i) {
+  auto process = [&](VTile<QT, KVT, D>& t, int i) {
+    if (i == patch_tile) {
+#pragma unroll
+      for (int u = 0; u < Tr::kLoads; ++u) {
+        patch_piece<KVT, D>(t.k[u], off0 + u * 1024, patch_row, tok_rows);
+        patch_piece<KVT, D>(t.v[u], off0 + u * 1024, patch_row, tok_rows + row_bytes<KVT, D>());
+      }
+    }
     float sc[Tr::kLoads];
     bool valid[Tr::kLoads];
 #pragma unroll
@@ -209,6 +222,8 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, co
     }
   }
 
+  if (writes) store_new_token<KVT>(a, token);
+
   // Combine the row groups.
   const float l_tot = groups_sum<LPR>(l_run);
 #pragma unroll
@@ -238,12 +253,17 @@ template <int QT, int KVT, int D, int NBUF>
 __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
   using Tr = ValuTraits<QT, KVT, D>;
   extern __shared__ int bt_lds[];
+  __shared__ __attribute__((aligned(16))) uint8_t tok_rows[kTokenRowsLds];
   const int j = item_of_workgroup(blockIdx.x);
   if (j >= a.num_items) return;
   const Item it = decode_item(j, a);
   const int ctx = min(a.context_lens[it.s], a.max_blocks * kBlock);
   const int start = it.p * a.part_blocks * kBlock;
+  const bool writes = owns_new_token(a, ctx, it.p);
+  TokenChunk token = {};
+  if (writes) token = load_new_token<QT, KVT, D>(a, it.s, it.g);
   if (ctx <= start) {
+    if (writes) store_new_token<KVT>(a, token);
     // Nothing in this partition. A whole sequence with no context writes zeros.
     const int lane = threadIdx.x;
     if (a.num_parts == 1 && lane < Tr::kLanesPerRow) {
@@ -254,9 +274,9 @@ __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
     return;
   }
   if (neighbour_shares_block(a, it.s, start / kBlock))
-    valu_item<QT, KVT, D, NBUF, kPolicyCached, false>(a, it, ctx, start, bt_lds);
+    valu_item<QT, KVT, D, NBUF, kPolicyCached, false>(a, it, ctx, start, bt_lds, tok_rows, writes, token);
   else
-    valu_item<QT, KVT, D, NBUF, kPolicyStream, true>(a, it, ctx, start, bt_lds);
+    valu_item<QT, KVT, D, NBUF, kPolicyStream, true>(a, it, ctx, start, bt_lds, tok_rows, writes, token);
 }
 
 template <int QT, int KVT, int D>

@@ -69,6 +69,65 @@ __device__ __forceinline__ u32x2 fp8x4_to_16(uint32_t w) {
   return r;
 }
 
+// OCP E4M3FN encoder, written from the format's definition: bias 7, 3 mantissa bits,
+// no infinities, S.1111.111 = NaN, largest finite 448, smallest subnormal 2^-9.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const float ax = fabsf(x);
+  if (ax != ax) return 0x7Fu | sign;                 // NaN
+  if (ax >= 448.0f) return 0x7Eu | sign;             // saturate (infinities too)
+  if (ax < 0.015625f) {                              // below 2^-6: multiples of 2^-9
+    return (uint32_t)__builtin_rintf(ax * 512.0f) | sign;   // exact scaling, then RNE
+  }
+  const uint32_t ab = __float_as_uint(ax);
+  const uint32_t r = ab + 0x7FFFFu + ((ab >> 20) & 1u);     // RNE at the 3rd mantissa bit
+  const uint32_t e = (r >> 23) - 127u + 7u;                   // biased E4M3 exponent, 1..15
+  return sign | (e << 3) | ((r >> 20) & 7u);
+}
+
+
+// 8 consecutive elements of a new token's K or V row (packed 16-bit values of type IT) in
+// the storage format of a cache of type KVT: a 16-bit cache takes the bits as they are
+// (all 16 bytes); an fp8 cache takes E4M3FN(fl32(x / scale)) of each element (IEEE fp32
+// division, round to nearest even, saturating, NaN kept; the 8 codes in the first two
+// dwords). Both the cache-write kernel and the fused decode step convert new tokens
+// through this function.
+template <int IT, int KVT>
+__device__ __forceinline__ u32x4 convert_cache_chunk(const u32x4 in, float scale) {
+  if constexpr (KVT == kFP8) {
+    u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pair = in[2 * w + e / 2];
+        const float x = (e & 1) ? hi16<IT>(pair) : lo16<IT>(pair);
+        packed |= e4m3_from_f32(x / scale) << (8 * e);
+      }
+      out[w] = packed;
+    }
+    return out;
+  } else {
+    return in;
+  }
+}
+
+// Stores a converted chunk (8 elements) at element index `elem` of the cache.
+template <int KVT>
+__device__ __forceinline__ void store_converted_chunk(const u32x4 c, void* cache, int64_t elem) {
+  if constexpr (KVT == kFP8)
+    *(u32x2*)((uint8_t*)cache + elem) = u32x2{c[0], c[1]};
+  else
+    *(u32x4*)((uint16_t*)cache + elem) = c;
+}
+
+template <int IT, int KVT>
+__device__ __forceinline__ void store_cache_chunk(const u32x4 in, void* cache, int64_t elem, float scale) {
+  store_converted_chunk<KVT>(convert_cache_chunk<IT, KVT>(in, scale), cache, elem);
+}
+
 // ---- cross-lane butterflies (VALU permlane swaps, gfx950) ------------------------------
 // Combine lane l with lane l^16 / l^32. permlane16_swap(v, v) hands each lane the pair
 // {v[l & ~16], v[l | 16]}; permlane32_swap(v, v) the pair {v[l & 31], v[(l & 31) + 32]}.

@@ -35,11 +35,15 @@ constexpr int kDecodeSmallLds = 2048;
 // Largest group-mode tile list (entries) a workgroup stages in LDS.
 constexpr int kMaxGroupListEntries = 2048;
 
+// LDS copy of one sequence's new token (K row then V row, storage format) in a fused step.
+constexpr int kTokenRowsLds = 512;
+
 // Dynamic LDS bytes of one matrix-core decode workgroup: per-wave K/V tile staging,
-// per-wave block-table slices, and in group mode the small area and the tile list.
+// per-wave new-token rows, per-wave block-table slices, and in group mode the small area
+// and the tile list.
 inline size_t mfma_decode_lds_bytes(int head_dim, int seqs_per_group, int part_blocks, bool group_mode) {
   const size_t tile = (size_t)2 * 16 * head_dim * 2;
-  return seqs_per_group * tile + (size_t)seqs_per_group * part_blocks * 4 +
+  return seqs_per_group * (tile + kTokenRowsLds) + (size_t)seqs_per_group * part_blocks * 4 +
          (group_mode ? kDecodeSmallLds + (size_t)2 * seqs_per_group * part_blocks * 4 : 0);
 }
 

@@ -93,6 +93,40 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
+def decode_step(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens, scale: float,
+                max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+                workspace: torch.Tensor | None = None, stream=None):
+    """Cache write of every sequence's new token, then decode attention, in one launch
+    (same results as reshape_and_cache followed by paged_attention_decode)."""
+    _dev(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens)
+    S, Hq, D = q.shape
+    NB, Hkv, P, D2 = k_cache.shape
+    if tuple(out.shape) != (S, Hq, D) or tuple(v_cache.shape) != tuple(k_cache.shape) or D2 != D:
+        raise ValueError("shape mismatch")
+    if tuple(key.shape) != (S, Hkv, D) or tuple(value.shape) != (S, Hkv, D):
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim]")
+    if out.dtype != q.dtype or v_cache.dtype != k_cache.dtype or key.dtype != q.dtype or value.dtype != q.dtype:
+        raise ValueError("dtype mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (S,):
+        raise ValueError("slot_mapping must be int64 [num_seqs]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables / context_lens shape mismatch")
+    need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.load().pkv_decode_step(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), key.data_ptr(), value.data_ptr(),
+        slot_mapping.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, Hq, Hkv, D, P, NB,
+        block_tables.shape[1], max_context_len, _dtype(q), _dtype(k_cache), scale, k_scale, v_scale, 0, 0, 0,
+        partition_size, ws_ptr, ws_bytes, _stream(stream))
+    _check("pkv_decode_step", st)
+    return out
+
+
 def reshape_and_cache(key, value, slot_mapping, k_cache, v_cache, k_scale: float = 1.0, v_scale: float = 1.0,
                       stream=None) -> None:
     """Write key/value [T, Hkv, D] rows into their slots of one layer's caches."""

@@ -88,3 +88,23 @@ def device_batch(cfg: WorkloadConfig, replica: int = 0):
                  "copy_pairs"):
         setattr(b, name, getattr(b, name).cuda())
     return b
+
+
+def gpu_fused_step(b, partition_size=None):
+    """The same step with the cache write fused into the decode launch."""
+    if len(b.copy_pairs):
+        pkv.copy_blocks([b.k_cache], [b.v_cache], b.copy_pairs)
+    out = torch.empty_like(b.q)
+    part = b.cfg.partition_size if partition_size is None else partition_size
+    pkv.decode_step(out, b.q, b.k_cache, b.v_cache, b.new_k, b.new_v, b.slot_mapping, b.block_tables, b.context_lens,
+                    b.scale, b.cfg.max_context_len, b.k_scale, b.v_scale, part)
+    return out
+
+
+def clone_batch(b):
+    """A copy of a device batch with its own caches (the step writes them)."""
+    import copy
+    c = copy.copy(b)
+    c.k_cache = b.k_cache.clone()
+    c.v_cache = b.v_cache.clone()
+    return c

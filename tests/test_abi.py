@@ -96,3 +96,21 @@ def test_cache_op_argument_errors():
     assert cb(None, ptrs, 1, 16, 2, 4096, 64, None) == -1
     nullp = (ctypes.c_void_p * 1)(None)
     assert cb(nullp, ptrs, 1, 16, 2, 4096, 64, None) == -1
+
+
+def test_fused_step_argument_errors():
+    lib = _lib.load()
+
+    def step(**kw):
+        a = dict(key=16, value=16, slots=16, kstride=0, vstride=0, S=4, Hq=8, Hkv=2)
+        a.update(kw)
+        return lib.pkv_decode_step(16, 16, 16, 16, a["key"], a["value"], a["slots"], 16, 16, a["S"], a["Hq"],
+                                   a["Hkv"], 128, 16, 64, 4, 64, _lib.PKV_BF16, _lib.PKV_BF16, 0.1, 1.0, 1.0, 0,
+                                   a["kstride"], a["vstride"], 0, None, 0, None)
+    assert step(key=None) == -1
+    assert step(slots=None) == -1
+    assert step(value=8) == -6                 # misaligned
+    assert step(kstride=100) == -2             # shorter than one token's rows (2 * 128)
+    assert step(kstride=260) == -6             # not a multiple of 8 elements
+    assert step(Hq=7) == -2
+    assert step(S=0) == 0
