@@ -82,8 +82,9 @@ int pkv_api_version(void);
  * Context-partition length, in tokens, that pkv_paged_attention_decode will use.
  * partition_size > 0 is validated and returned as is (it must be a multiple of 16);
  * 0 asks the library to choose: one partition per sequence when num_seqs *
- * num_kv_heads work items already fill the GPU, otherwise the longest multiple of
- * 256 tokens that gives about 2048 items. Returns a negative pkv_status on bad input.
+ * num_kv_heads work items already fill the GPU (1024 or more), otherwise the longest
+ * multiple of 256 tokens that gives about 1024 items. Returns a negative pkv_status on
+ * bad input.
  */
 int pkv_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_context_len, int partition_size);
 

@@ -42,7 +42,8 @@ def test_partition_choice():
     assert lib.pkv_decode_partition_tokens(256, 8, 768, 0) == 768
     assert lib.pkv_decode_partition_tokens(64, 32, 2048, 0) == 2048
     # few items: split long contexts
-    assert lib.pkv_decode_partition_tokens(8, 8, 32768, 0) == 1024
+    assert lib.pkv_decode_partition_tokens(8, 8, 32768, 0) == 2048
+    assert lib.pkv_decode_partition_tokens(64, 8, 4096, 0) == 2048      # 512 items: two partitions each
     assert lib.pkv_decode_partition_tokens(8, 8, 32768, 512) == 512
     assert lib.pkv_decode_partition_tokens(4, 2, 37, 0) == 48
     assert lib.pkv_decode_partition_tokens(8, 8, 100, 24) == -2      # not a multiple of 16

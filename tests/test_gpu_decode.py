@@ -181,15 +181,20 @@ def test_fp8_cache_over_every_finite_code():
 
 @pytest.mark.parametrize("partition", [0, 32])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("G,kv_dtype,tail", [(2, "bf16", 40), (4, "bf16", 40), (4, "fp8_e4m3", 40), (8, "bf16", 40),
-                                             (4, "bf16", 0), (2, "fp8_e4m3", 17)])
-def test_sharing_groups_match_oracle(G, kv_dtype, tail, D, partition):
+@pytest.mark.parametrize("G,kv_dtype,tail,width,S", [(2, "bf16", 40, 4, 16), (4, "bf16", 40, 4, 16),
+                                                     (4, "fp8_e4m3", 40, 4, 16), (8, "bf16", 40, 4, 16),
+                                                     (4, "bf16", 0, 4, 16), (2, "fp8_e4m3", 17, 4, 16),
+                                                     (4, "bf16", 30, 2, 10), (16, "bf16", 40, 4, 8)])
+def test_sharing_groups_match_oracle(G, kv_dtype, tail, width, S, D, partition):
     # Workgroups of neighbouring sequences that share blocks read each shared block once
     # for all of them; every sharing pattern the beam generator makes (whole prefixes,
     # tails shared by children of one parent, no private tail at all) against the oracle.
-    cfg = WorkloadConfig(name=f"groups_G{G}_{kv_dtype}_D{D}_t{tail}", num_seqs=16, num_q_heads=2 * G, num_kv_heads=2,
-                         head_dim=D, num_blocks=2048, seed=31 + G + tail, dtype="bf16", kv_dtype=kv_dtype,
-                         ctx=("beam", 96, 0, tail, 4), max_context_len=96 + tail + 1,
+    # Width-2 beams in workgroups of 4 put two requests in one workgroup and leave a
+    # partial last workgroup (independent mode); 16 heads per kv head leave one sequence
+    # per workgroup (shared blocks then take the cached path).
+    cfg = WorkloadConfig(name=f"groups_G{G}_{kv_dtype}_D{D}_t{tail}_w{width}", num_seqs=S, num_q_heads=2 * G,
+                         num_kv_heads=2, head_dim=D, num_blocks=2048, seed=31 + G + tail, dtype="bf16",
+                         kv_dtype=kv_dtype, ctx=("beam", 96, 0, tail, width), max_context_len=96 + tail + 1,
                          kv_scale=(1 / 128 if kv_dtype == "fp8_e4m3" else 1.0))
     b = device_batch(cfg)
     h = HostBatch(b)
