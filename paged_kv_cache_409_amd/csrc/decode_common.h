@@ -170,19 +170,6 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, POLICY));
 }
 
-// True when block `idx` of sequence s's table is also the block at the same logical
-// index of the previous or next sequence in the batch. That is the layout of beams (or
-// parallel samples) forked from one prompt: they share its blocks and sit next to each
-// other in the batch. idx must be < max_blocks.
-__device__ __forceinline__ bool neighbour_shares_block(const DecodeArgs& a, int s, int idx) {
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + idx;
-  const int mine = bt[0];
-  bool shared = false;
-  if (s > 0) shared = shared || bt[-a.max_blocks] == mine;
-  if (s + 1 < a.num_seqs) shared = shared || bt[a.max_blocks] == mine;
-  return shared;
-}
-
 // Two waves share each SIMD and the older one wins instruction arbitration, so without
 // help it runs ahead and finishes long before its neighbour, leaving the memory system
 // under-fed at the end of the launch. A wave that streams private blocks therefore

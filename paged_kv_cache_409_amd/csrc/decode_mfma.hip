@@ -535,17 +535,35 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
   const int w = threadIdx.x / kWave;
   const int start = it.p * a.part_blocks * kBlock;
 
+  // The values the first decisions need are independent loads, issued together (one
+  // memory latency rather than a chain): this wave's context length and the block ids at
+  // logical block i0 of its sequence and of the sequences on either side, and for the
+  // group check the same of every sequence of the group (indices clamped into the batch).
+  const int i0 = start / kBlock;
+  const int max_tokens = a.max_blocks * kBlock;
+  const int64_t mb = a.max_blocks;
+  const int s = it.s + w;
+  const int s_own = min(s, a.num_seqs - 1);
+  const int ctx = min(a.context_lens[s_own], max_tokens);
+  const int mine = a.block_tables[s_own * mb + i0];
+  const int prev = a.block_tables[max(s_own - 1, 0) * mb + i0];
+  const int next = a.block_tables[min(s_own + 1, a.num_seqs - 1) * mb + i0];
+
   // Group mode when every sequence of the group has tokens in this partition and another
   // sequence reads the first sequence's first block of it. Every wave evaluates the same
   // condition, so the whole workgroup takes the same branch.
   if (a.group_mode_ok && it.s + B <= a.num_seqs) {
-    const int i0 = start / kBlock;
-    const int first = a.block_tables[(int64_t)it.s * a.max_blocks + i0];
+    const int first0 = a.block_tables[it.s * mb + i0];
     bool all_live = true, shares = false;
-    for (int b = 0; b < B; ++b) {
-      const int c = min(a.context_lens[it.s + b], a.max_blocks * kBlock);
-      all_live = all_live && c > start;
-      if (b > 0) shares = shares || a.block_tables[(int64_t)(it.s + b) * a.max_blocks + i0] == first;
+#pragma unroll
+    for (int b = 0; b < kMaxSeqsPerGroup; ++b) {
+      const int sb = min(it.s + b, a.num_seqs - 1);
+      const int c = a.context_lens[sb];
+      const int f = a.block_tables[sb * mb + i0];
+      if (b < B) {
+        all_live = all_live && min(c, max_tokens) > start;
+        if (b > 0) shares = shares || f == first0;
+      }
     }
     if (all_live && shares) {
       mfma_group<QT, KVT, D>(a, it.s, it.g, it.p, start, smem);
@@ -554,9 +572,7 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
   }
 
   // Independent mode: wave w runs sequence it.s + w with its own LDS areas.
-  const int s = it.s + w;
   if (s >= a.num_seqs) return;
-  const int ctx = min(a.context_lens[s], a.max_blocks * kBlock);
   const bool writes = owns_new_token(a, ctx, it.p);
   TokenChunk token = {};
   if (writes) token = load_new_token<QT, KVT, D>(a, s, it.g);
@@ -574,12 +590,9 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
   uint8_t* lds = smem + w * Tr::kLdsBytes;
   uint8_t* tok_rows = smem + B * Tr::kLdsBytes + w * kTokenRowsLds;
   int* bt_lds = (int*)(smem + B * (Tr::kLdsBytes + kTokenRowsLds)) + w * a.part_blocks;
-  // Blocks shared with a neighbouring sequence: cached loads (the other readers hit L2),
-  // two tiles in flight, default priority, K straight into registers (these items are
-  // bound by per-block latency more than by HBM). Private blocks stream, with K through
-  // LDS; a whole context in one partition does best with one tile in flight per wave, a
-  // split context (more items than wave slots) with two.
-  if (neighbour_shares_block(a, s, start / kBlock))
+  // Does the previous or next sequence of the batch read this sequence's first block?
+  const bool shared = (s > 0 && prev == mine) || (s + 1 < a.num_seqs && next == mine);
+  if (shared)
     mfma_single<QT, KVT, D, 2, kPolicyCached, false, false>(a, s, it.g, it.p, ctx, start, bt_lds, lds, tok_rows, writes, token);
   else if (a.num_parts > 1)
     mfma_single<QT, KVT, D, 2, kPolicyStream, true, true>(a, s, it.g, it.p, ctx, start, bt_lds, lds, tok_rows, writes, token);

@@ -257,8 +257,15 @@ __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
   const int j = item_of_workgroup(blockIdx.x);
   if (j >= a.num_items) return;
   const Item it = decode_item(j, a);
-  const int ctx = min(a.context_lens[it.s], a.max_blocks * kBlock);
   const int start = it.p * a.part_blocks * kBlock;
+  // The context length and the block ids at the partition's first logical block of this
+  // sequence and its two neighbours, loaded at once (clamped into the batch).
+  const int i0 = start / kBlock;
+  const int s_prev = max(it.s - 1, 0), s_next = min(it.s + 1, a.num_seqs - 1);
+  const int ctx = min(a.context_lens[it.s], a.max_blocks * kBlock);
+  const int first_prev = a.block_tables[(int64_t)s_prev * a.max_blocks + i0];
+  const int first = a.block_tables[(int64_t)it.s * a.max_blocks + i0];
+  const int first_next = a.block_tables[(int64_t)s_next * a.max_blocks + i0];
   const bool writes = owns_new_token(a, ctx, it.p);
   TokenChunk token = {};
   if (writes) token = load_new_token<QT, KVT, D>(a, it.s, it.g);
@@ -273,7 +280,8 @@ __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
     }
     return;
   }
-  if (neighbour_shares_block(a, it.s, start / kBlock))
+  const bool shared = (it.s > 0 && first_prev == first) || (it.s + 1 < a.num_seqs && first_next == first);
+  if (shared)
     valu_item<QT, KVT, D, NBUF, kPolicyCached, false>(a, it, ctx, start, bt_lds, tok_rows, writes, token);
   else
     valu_item<QT, KVT, D, NBUF, kPolicyStream, true>(a, it, ctx, start, bt_lds, tok_rows, writes, token);
