@@ -115,3 +115,52 @@ def merge_partitions(ms, ls, os_):
     num = sum(w[p][:, None] * os_[p] for p in range(len(os_)))
     den = (w * np.asarray(ls)).sum(axis=0)
     return num / den[:, None]
+
+
+# --- prefill chunks ------------------------------------------------------------------
+# Long prompts are cut into chunks that are run between decode steps
+# ("vLLM推理引擎PagedAttention原理与性能优化实战", §六); the prefill phase is the
+# compute-bound part of a request's latency ("vLLM 推理优化技术深度调研报告", 维度一.3
+# 公式 5). The pages state no formula for a chunk. The plain reading taken here: a chunk
+# of n new tokens is the last n positions of the sequence's context, its K/V are already
+# in the cache, and new token i (position ctx - n + i) attends to positions 0 .. ctx - n + i,
+# i.e. ordinary causal attention over the whole context so far.
+
+def paged_prefill_attention(q_bits, k_cache_bits, v_cache_bits, block_tables, context_lens,
+                            query_start_loc, scale, q_format: str, kv_format: str,
+                            k_scale: float = 1.0, v_scale: float = 1.0, seqs=None) -> np.ndarray:
+    """Causal attention of each sequence's chunk of new tokens over its paged context.
+
+    q_bits          [T, Hq, D]        raw bits of the new tokens' queries, sequences back to back
+    query_start_loc [S + 1]           sequence s owns rows [qsl[s], qsl[s+1]) of q
+    context_lens    [S]               int, context length after the chunk (chunk included)
+    Returns float64 [T, Hq, D]; rows of sequences outside `seqs` (default: all) stay 0.
+    """
+    q_bits = np.asarray(q_bits)
+    T, Hq, D = q_bits.shape
+    Hkv = k_cache_bits.shape[1]
+    if Hq % Hkv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    G = Hq // Hkv
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    S = len(context_lens)
+    if len(qsl) != S + 1 or qsl[0] != 0 or qsl[-1] > T or np.any(np.diff(qsl) < 0):
+        raise ValueError("query_start_loc must rise from 0 and end within the query rows")
+    scale = float(np.float32(scale))
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for s in (range(S) if seqs is None else seqs):
+        ctx, first, n = int(context_lens[s]), int(qsl[s]), int(qsl[s + 1] - qsl[s])
+        if n > ctx:
+            raise ValueError(f"sequence {s}: chunk of {n} tokens exceeds its context of {ctx}")
+        if n == 0:
+            continue
+        prefix = ctx - n
+        qs = formats.to_f64(q_bits[first:first + n], q_format)          # [n, Hq, D]
+        for g in range(Hkv):
+            K = decode_kv(gather_sequence(k_cache_bits, block_tables[s], ctx, g), kv_format, k_scale)
+            V = decode_kv(gather_sequence(v_cache_bits, block_tables[s], ctx, g), kv_format, v_scale)
+            for i in range(n):
+                seen = prefix + i + 1
+                out[first + i, g * G:(g + 1) * G] = softmax_attention(qs[i, g * G:(g + 1) * G],
+                                                                       K[:seen], V[:seen], scale)
+    return out

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from oracle import attention
-from workloads import CONFIGS, make_batch, make_layout
+from workloads import ALL_CONFIGS, CONFIGS, make_batch, make_layout
 from workloads.blocks import BlockPool, PoolExhausted, Sequence
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -77,34 +77,45 @@ def test_pool_exhaustion_is_a_clean_error_and_free_returns_blocks():
     assert pool.num_free == 2
 
 
-@pytest.mark.parametrize("name", list(CONFIGS))
+@pytest.mark.parametrize("name", list(ALL_CONFIGS))
 def test_layout_invariants(name):
-    cfg = CONFIGS[name]
+    cfg = ALL_CONFIGS[name]
     lay = make_layout(cfg)
     P = cfg.block_size
     S = cfg.num_seqs
+    qsl = lay.query_start_loc
     assert lay.block_tables.shape == (S, cfg.max_blocks_per_seq)
     assert (lay.context_lens >= 1).all() and (lay.context_lens <= cfg.max_context_len).all()
+    assert qsl.shape == (S + 1,) and qsl[0] == 0 and len(lay.slot_mapping) == qsl[-1]
+    n_new = np.diff(qsl)
+    assert (n_new >= 1).all() and (n_new <= lay.context_lens).all()
+    if not cfg.chunk:
+        assert (n_new == 1).all()
+    written = set(lay.copy_pairs[:, 1].tolist())
     owner = {}
     for s in range(S):
-        n = -(-int(lay.context_lens[s]) // P)
+        ctx, n = int(lay.context_lens[s]), int(n_new[s])
+        nb = -(-ctx // P)
         row = lay.block_tables[s]
-        assert (row[n:] == lay.poison_block).all()
-        assert lay.poison_block not in row[:n]
-        # the new token's slot is the last logical position of the sequence
-        assert attention.physical_slot(row, int(lay.context_lens[s]) - 1, P) == divmod(int(lay.slot_mapping[s]), P)
-        for j in range(n):
+        assert (row[nb:] == lay.poison_block).all()
+        assert lay.poison_block not in row[:nb]
+        # the new tokens' slots are the last n logical positions of the sequence
+        for k in range(n):
+            slot = int(lay.slot_mapping[qsl[s] + k])
+            assert attention.physical_slot(row, ctx - n + k, P) == divmod(slot, P)
+            assert not lay.history_valid[slot // P, slot % P]      # stale before the step
+        for j in range(nb):
             owner.setdefault(int(row[j]), set()).add(s)
-        # history slots hold data, the new token's slot is stale before the step
-        for t in range(int(lay.context_lens[s]) - 1):
+        # history slots hold data
+        for t in range(ctx - n):
             b, o = attention.physical_slot(row, t, P)
-            if b not in set(lay.copy_pairs[:, 1].tolist()):
+            if b not in written:
                 assert lay.history_valid[b, o]
     assert not lay.history_valid[lay.poison_block].any()
     # a block written this step (holding a new token) belongs to one sequence only
     for s in range(S):
-        b = int(lay.slot_mapping[s]) // P
-        assert owner[b] == {s}
+        for slot in lay.slot_mapping[qsl[s]:qsl[s + 1]]:
+            assert owner[int(slot) // P] == {s}
     dst = lay.copy_pairs[:, 1]
     assert len(set(dst.tolist())) == len(dst)
     assert not set(dst.tolist()) & set(lay.copy_pairs[:, 0].tolist())

@@ -3,5 +3,5 @@
 Holds only random draws and block bookkeeping; none of the attention,
 quantisation or cache-write arithmetic lives here.
 """
-from .configs import CONFIGS, WorkloadConfig  # noqa: F401
+from .configs import ALL_CONFIGS, CONFIGS, PREFILL_CONFIGS, WorkloadConfig  # noqa: F401
 from .gen import Batch, Layout, make_batch, make_layout  # noqa: F401

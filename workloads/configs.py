@@ -24,10 +24,13 @@ class WorkloadConfig:
     dtype: str                     # q / new-token dtype: "f16" | "bf16"
     kv_dtype: str                  # cache dtype: "f16" | "bf16" | "fp8_e4m3"
     ctx: tuple                     # ("fixed", [..]) | ("uniform", lo, hi) | ("beam", prompt, tail_lo, tail_hi, width)
+                                   # context length after the step, new tokens included
     max_context_len: int
     block_size: int = 16
     partition_size: int = 0        # 0: the library picks
     kv_scale: float = 1.0          # per-tensor scale of an fp8 cache (both K and V)
+    chunk: tuple = ()              # new tokens per sequence this step: () = 1 (a decode step),
+                                   # ("fixed", n) or ("uniform", lo, hi) (a prefill chunk, at most the context)
     description: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -73,3 +76,21 @@ BEAM_COW = WorkloadConfig(
                 "copy-on-write of shared partial blocks, fp8-e4m3 KV (per-tensor scale 1/128), bf16 q")
 
 CONFIGS = {c.name: c for c in (TINY, LLAMA2_7B, LLAMA2_70B_GQA, LONG_COT, BEAM_COW)}
+
+# Prefill chunks ("vLLM推理引擎PagedAttention原理与性能优化实战", §六): each sequence brings a
+# chunk of new tokens that attend causally to its cached context and to each other.
+PREFILL_TINY = WorkloadConfig(
+    name="prefill_tiny", num_seqs=4, num_q_heads=4, num_kv_heads=2, head_dim=64, num_blocks=64,
+    seed=40906, dtype="f16", kv_dtype="f16", ctx=("fixed", [5, 16, 37, 90]), max_context_len=90,
+    chunk=("uniform", 1, 40),
+    description="4 seqs, ctx {5,16,37,90}, chunks U[1,40], 4 q / 2 kv heads, D 64, fp16, 64-block pool")
+
+PREFILL_70B_GQA = WorkloadConfig(
+    name="prefill_70b_gqa", num_seqs=8, num_q_heads=64, num_kv_heads=8, head_dim=128, num_blocks=4096,
+    seed=40907, dtype="bf16", kv_dtype="bf16", ctx=("uniform", 512, 4096), max_context_len=4096,
+    chunk=("fixed", 512),
+    description="Llama-2-70B GQA layer, chunked prefill: 8 seqs, 512-token chunks after cached "
+                "prefixes of 0-3584 tokens (ctx U[512,4096]), 64 q / 8 kv heads, D 128, bf16")
+
+PREFILL_CONFIGS = {c.name: c for c in (PREFILL_TINY, PREFILL_70B_GQA)}
+ALL_CONFIGS = {**CONFIGS, **PREFILL_CONFIGS}

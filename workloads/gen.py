@@ -47,11 +47,12 @@ ELEM_BYTES = {"f16": 2, "bf16": 2, "fp8_e4m3": 1}
 class Layout:
     """Where every token of a decode batch lives (host numpy arrays)."""
     block_tables: np.ndarray      # int32 [S, max_blocks], padded with poison_block
-    context_lens: np.ndarray      # int32 [S], after the step's new token
-    slot_mapping: np.ndarray      # int64 [S], slot of the step's new token
+    context_lens: np.ndarray      # int32 [S], after the step's new tokens
+    slot_mapping: np.ndarray      # int64 [T], slot of each of the step's new tokens
     copy_pairs: np.ndarray        # int64 [Pn, 2], copy-on-write (src, dst) of this step
     history_valid: np.ndarray     # bool [NB, P], slots holding KV before the step
     poison_block: int
+    query_start_loc: np.ndarray   # int32 [S + 1]: sequence s's new tokens are rows [qsl[s], qsl[s+1])
 
 
 def _seed_streams(cfg: WorkloadConfig, replica: int, n: int):
@@ -59,8 +60,21 @@ def _seed_streams(cfg: WorkloadConfig, replica: int, n: int):
     return [np.random.default_rng(s) for s in ss.spawn(n)]
 
 
+def _chunk_lens(cfg: WorkloadConfig, ctx, rng) -> np.ndarray:
+    """New tokens per sequence this step (1 for a decode step), never more than the context."""
+    if not cfg.chunk:
+        return np.ones(len(ctx), dtype=np.int64)
+    if cfg.chunk[0] == "fixed":
+        n = np.full(len(ctx), int(cfg.chunk[1]), dtype=np.int64)
+    elif cfg.chunk[0] == "uniform":
+        n = rng.integers(cfg.chunk[1], cfg.chunk[2] + 1, size=len(ctx))
+    else:
+        raise ValueError(f"unknown chunk kind {cfg.chunk[0]!r}")
+    return np.minimum(n, np.asarray(ctx, dtype=np.int64))
+
+
 def make_layout(cfg: WorkloadConfig, replica: int = 0) -> Layout:
-    rng_ctx, rng_place, rng_tail, rng_parent = _seed_streams(cfg, replica, 4)
+    rng_ctx, rng_place, rng_tail, rng_parent, rng_chunk = _seed_streams(cfg, replica, 5)
     P = cfg.block_size
     pool = BlockPool(cfg.num_blocks, P, order=rng_place.permutation(cfg.num_blocks))
     poison = pool.allocate()
@@ -74,13 +88,17 @@ def make_layout(cfg: WorkloadConfig, replica: int = 0) -> Layout:
             ctx = rng_ctx.integers(cfg.ctx[1], cfg.ctx[2] + 1, size=cfg.num_seqs)
         if len(ctx) != cfg.num_seqs:
             raise ValueError("context list does not match num_seqs")
-        for c in ctx:
+        new_tokens = _chunk_lens(cfg, ctx, rng_chunk)
+        for c, q in zip(ctx, new_tokens):
             seq = Sequence(pool)
-            slots, copies = seq.extend(max(int(c) - 1, 0))
+            slots, copies = seq.extend(max(int(c) - int(q), 0))   # the history before the step
             assert not copies
             history.append(slots)
             live.append(seq)
     elif kind == "beam":
+        if cfg.chunk:
+            raise ValueError("beam workloads decode one token per sequence")
+        new_tokens = None
         prompt, tail_lo, tail_hi, width = cfg.ctx[1:]
         if cfg.num_seqs % width:
             raise ValueError("num_seqs must be a multiple of the beam width")
@@ -110,13 +128,18 @@ def make_layout(cfg: WorkloadConfig, replica: int = 0) -> Layout:
         valid[np.asarray(slots, dtype=np.int64)] = True
 
     S = len(live)
-    slot_mapping = np.empty(S, dtype=np.int64)
+    if new_tokens is None:
+        new_tokens = np.ones(S, dtype=np.int64)
+    query_start_loc = np.zeros(S + 1, dtype=np.int32)
+    query_start_loc[1:] = np.cumsum(new_tokens)
+    slot_mapping = np.empty(int(query_start_loc[-1]), dtype=np.int64)
     pairs = []
     for i, seq in enumerate(live):
-        slot, copy = seq.append_slot()
-        slot_mapping[i] = slot
-        if copy is not None:
-            pairs.append(copy)
+        for k in range(int(new_tokens[i])):
+            slot, copy = seq.append_slot()
+            slot_mapping[query_start_loc[i] + k] = slot
+            if copy is not None:
+                pairs.append(copy)
     block_tables = np.full((S, cfg.max_blocks_per_seq), poison, dtype=np.int32)
     context_lens = np.empty(S, dtype=np.int32)
     for i, seq in enumerate(live):
@@ -126,7 +149,7 @@ def make_layout(cfg: WorkloadConfig, replica: int = 0) -> Layout:
         context_lens[i] = seq.num_tokens
     copy_pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
     return Layout(block_tables, context_lens, slot_mapping, copy_pairs,
-                  valid.reshape(cfg.num_blocks, P), poison)
+                  valid.reshape(cfg.num_blocks, P), poison, query_start_loc)
 
 
 @dataclass
@@ -134,15 +157,16 @@ class Batch:
     """One decode step's inputs, as torch tensors on one device."""
     cfg: WorkloadConfig
     layout: Layout
-    q: torch.Tensor              # [S, Hq, D] dtype
-    new_k: torch.Tensor          # [S, Hkv, D] dtype
-    new_v: torch.Tensor          # [S, Hkv, D] dtype
+    q: torch.Tensor              # [T, Hq, D] dtype: the step's new tokens (T = S for a decode step)
+    new_k: torch.Tensor          # [T, Hkv, D] dtype
+    new_v: torch.Tensor          # [T, Hkv, D] dtype
     k_cache: torch.Tensor        # [NB, Hkv, P, D] kv dtype (uint8 codes for fp8)
     v_cache: torch.Tensor
     block_tables: torch.Tensor   # int32 [S, max_blocks]
     context_lens: torch.Tensor   # int32 [S]
-    slot_mapping: torch.Tensor   # int64 [S]
+    slot_mapping: torch.Tensor   # int64 [T]
     copy_pairs: torch.Tensor     # int64 [Pn, 2]
+    query_start_loc: torch.Tensor  # int32 [S + 1]
 
     @property
     def scale(self) -> float:
@@ -192,7 +216,7 @@ def make_pool(cfg: WorkloadConfig, valid: np.ndarray, device, seed: int) -> torc
 
 def make_batch(cfg: WorkloadConfig, device="cpu", replica: int = 0) -> Batch:
     lay = make_layout(cfg, replica)
-    S, Hq, Hkv, D = len(lay.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    S, Hq, Hkv, D = int(lay.query_start_loc[-1]), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
     base = (cfg.seed * 1000 + replica) * 16
     dt = TORCH_DTYPE[cfg.dtype]
     q = _normal((S, Hq, D), dt, device, base + 1)
@@ -202,7 +226,7 @@ def make_batch(cfg: WorkloadConfig, device="cpu", replica: int = 0) -> Batch:
     v_cache = make_pool(cfg, lay.history_valid, device, base + 5)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
     return Batch(cfg, lay, q, new_k, new_v, k_cache, v_cache, t(lay.block_tables), t(lay.context_lens),
-                 t(lay.slot_mapping), t(lay.copy_pairs))
+                 t(lay.slot_mapping), t(lay.copy_pairs), t(lay.query_start_loc))
 
 
 def kv_bytes_logical(cfg: WorkloadConfig, context_lens) -> int:
