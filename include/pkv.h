@@ -8,11 +8,12 @@
  *   pkv_reshape_and_cache       write each new token's K/V row into its cache slot
  *   pkv_copy_blocks             copy-on-write copies of whole KV blocks
  *   pkv_decode_step             cache write + attention of one decode step, one launch
+ *   pkv_paged_attention_prefill causal attention of prefill chunks over the paged cache
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Pointers named *_cache, q, out, key, value, block_tables, context_lens,
- *   slot_mapping, src_dst_pairs and workspace are DEVICE pointers; every other
+ *   query_start_loc, slot_mapping, src_dst_pairs and workspace are DEVICE pointers; every other
  *   pointer is a host pointer. All tensors are dense, row-major, in the shapes
  *   given below, and 16-byte aligned.
  * - The caller allocates and owns every buffer, including the workspace. The
@@ -164,6 +165,43 @@ int pkv_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
                     int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
                     int64_t q_seq_stride, int64_t key_stride, int64_t value_stride, int partition_size,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Attention of prefill chunks over a paged KV cache. Long prompts are cut into chunks
+ * that run between decode steps ("vLLM推理引擎PagedAttention原理与性能优化实战", §六);
+ * the pages give no formula for a chunk, and this library takes the plain reading: a
+ * chunk of n_s new tokens is the last n_s positions of sequence s's context, its K/V are
+ * already in the cache (the caller runs pkv_reshape_and_cache for the chunk's
+ * num_tokens rows first), and new token i, at position p = context_lens[s] - n_s + i,
+ * attends causally to positions 0 .. p:
+ *   out[r, h, :] = softmax(scale * K_s[0..p] q[r, h]) V_s[0..p],   r = query_start_loc[s] + i
+ * with K_s, V_s and the kv head of h as for pkv_paged_attention_decode, accumulated in
+ * fp32 and rounded (nearest even) to q's dtype. With n_s = 1 for every sequence this is
+ * a decode step.
+ *
+ *   out            [num_tokens, num_q_heads, head_dim]        q_dtype, dense (written)
+ *   q              [num_tokens, num_q_heads, head_dim]        q_dtype; token stride
+ *                  q_token_stride elements (0 = num_q_heads * head_dim)
+ *   query_start_loc[num_seqs + 1] int32: sequence s owns rows [qsl[s], qsl[s+1]) of q
+ *                  and out; non-decreasing, qsl[num_seqs] <= num_tokens
+ *   context_lens   [num_seqs] int32: context length after the chunk (chunk included),
+ *                  at least n_s and at most max_blocks_per_seq * 16
+ *   max_query_len  upper bound of every n_s (host-side hint; sets the grid)
+ *   scale          logit scale, finite and > 0
+ * Every other argument is as for pkv_paged_attention_decode. No workspace is needed.
+ *
+ * Rows outside every sequence's range are not written. A sequence whose offsets fall
+ * outside [0, num_tokens] is skipped; a chunk longer than max_query_len or than its
+ * context is cut to the shorter, and only its first rows are written.
+ * Supported: head_dim 64 or 128; any group size; block_size 16; matrix cores throughout.
+ */
+int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                const int32_t* query_start_loc,
+                                int num_seqs, int num_tokens, int num_q_heads, int num_kv_heads, int head_dim,
+                                int block_size, int64_t num_blocks, int max_blocks_per_seq, int max_query_len,
+                                int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
+                                int64_t q_token_stride, void* stream);
 
 /*
  * Write the K and V rows of num_tokens new tokens into their cache slots

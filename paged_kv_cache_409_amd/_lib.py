@@ -37,6 +37,12 @@ SIGNATURES = {
         _c_int, _c_int, _c_f, _c_f, _c_f,              # q_dtype kv_dtype scale k_scale v_scale
         _c_i64, _c_i64, _c_i64, _c_int,                # q_seq_stride key_stride value_stride partition_size
         _c_p, _c_sz, _c_p]),                           # workspace workspace_bytes stream
+    "pkv_paged_attention_prefill": (_c_int, [
+        _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,      # out q k_cache v_cache block_tables context_lens qsl
+        _c_int, _c_int, _c_int, _c_int, _c_int,        # num_seqs num_tokens num_q_heads num_kv_heads head_dim
+        _c_int, _c_i64, _c_int, _c_int,                # block_size num_blocks max_blocks_per_seq max_query_len
+        _c_int, _c_int, _c_f, _c_f, _c_f,              # q_dtype kv_dtype scale k_scale v_scale
+        _c_i64, _c_p]),                                # q_token_stride stream
     "pkv_reshape_and_cache": (_c_int, [
         _c_p, _c_p, _c_p, _c_p, _c_p,                  # key value slot_mapping k_cache v_cache
         _c_int, _c_int, _c_int, _c_int, _c_i64,        # num_tokens num_kv_heads head_dim block_size num_blocks

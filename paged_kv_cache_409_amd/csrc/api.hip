@@ -259,6 +259,64 @@ int pkv_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
                      k_scale, v_scale, q_seq_stride, partition_size, &tok, workspace, workspace_bytes, stream);
 }
 
+int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                const int32_t* query_start_loc,
+                                int num_seqs, int num_tokens, int num_q_heads, int num_kv_heads, int head_dim,
+                                int block_size, int64_t num_blocks, int max_blocks_per_seq, int max_query_len,
+                                int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
+                                int64_t q_token_stride, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_query_len < 0)
+    return PKV_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (!is16bit(q_dtype)) return PKV_ERR_DTYPE;
+  if (kv_dtype != q_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (block_size != 16 || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
+  if (!(std::isfinite(scale) && scale > 0.f)) return PKV_ERR_SHAPE;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+  if (fp8 && !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return PKV_ERR_SHAPE;
+  if (q_token_stride == 0) q_token_stride = (int64_t)num_q_heads * head_dim;
+  if (q_token_stride < (int64_t)num_q_heads * head_dim) return PKV_ERR_SHAPE;
+  const int group = num_q_heads / num_kv_heads;
+  const long long rows = (long long)max_query_len * group;
+  if (rows > (1LL << 30) || (long long)num_tokens * num_q_heads > (1LL << 40)) return PKV_ERR_SHAPE;
+  const long long row_tiles = (rows + pkv::kPrefillRows - 1) / pkv::kPrefillRows;
+  const long long items = (long long)num_kv_heads * num_seqs * row_tiles;
+  if (items > (1LL << 31) - 8) return PKV_ERR_SHAPE;
+  if (items == 0 || num_tokens == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || q_token_stride % 8 != 0)
+    return PKV_ERR_ALIGN;
+
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.q_token_stride = q_token_stride;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_query_len = max_query_len;
+  a.row_tiles = (int)row_tiles;
+  a.num_items = (int)items;
+  a.qk_scale_log2 = scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
+  a.v_scale = fp8 ? v_scale : 1.0f;
+  const int qt = q_dtype == PKV_BF16 ? pkv::kBF16 : pkv::kF16;
+  const int kt = fp8 ? pkv::kFP8 : qt;
+  return hip_status(pkv::launch_prefill_mfma(a, qt, kt, head_dim, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int pkv_reshape_and_cache(const void* key, const void* value, const int64_t* slot_mapping,
                           void* k_cache, void* v_cache,
                           int num_tokens, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,

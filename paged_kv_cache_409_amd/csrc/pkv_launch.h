@@ -47,6 +47,36 @@ inline size_t mfma_decode_lds_bytes(int head_dim, int seqs_per_group, int part_b
          (group_mode ? kDecodeSmallLds + (size_t)2 * seqs_per_group * part_blocks * 4 : 0);
 }
 
+// One launch of the prefill-chunk kernel. Work item = (kv head, sequence, tile of
+// kPrefillRows query rows); the rows of a sequence and kv head are its new tokens x the
+// G query heads of the group, token-major.
+struct PrefillArgs {
+  void* out;                      // [T, Hq, D] q dtype, contiguous
+  const void* q;                  // [T, Hq, D] q dtype, token stride q_token_stride elements
+  const void* k_cache;            // [NB, Hkv, 16, D]
+  const void* v_cache;            // [NB, Hkv, 16, D]
+  const int32_t* block_tables;    // [S, max_blocks]
+  const int32_t* context_lens;    // [S], after the chunk
+  const int32_t* query_start_loc; // [S + 1]
+  int64_t q_token_stride;
+  int64_t num_blocks;
+  int num_seqs, num_tokens, num_q_heads, num_kv_heads, group;
+  int max_blocks;                 // block-table row length
+  int max_query_len;              // longest chunk the launch covers
+  int row_tiles;                  // ceil(max_query_len * group / kPrefillRows)
+  int num_items;                  // num_kv_heads * num_seqs * row_tiles
+  float qk_scale_log2;            // scale * log2(e) (* k_scale for an fp8 cache)
+  float v_scale;                  // 1, or v_scale for an fp8 cache
+};
+
+// Prefill workgroup: 4 wavefronts x 32 query rows, keys taken 64 (four cache blocks) at
+// a time.
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillCols = 32;
+constexpr int kPrefillRows = kPrefillWaves * kPrefillCols;
+constexpr int kPrefillKeys = 64;
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int q_type, int kv_type, int head_dim, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int q_type, int kv_type, int head_dim, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, int q_type, int kv_type, int head_dim, hipStream_t s);
 hipError_t launch_decode_reduce(const ReduceArgs& a, int q_type, int head_dim, hipStream_t s);

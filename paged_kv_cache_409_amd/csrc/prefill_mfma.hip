@@ -1,0 +1,311 @@
+// Paged attention of prefill chunks on gfx950 matrix cores.
+//
+// The method (what is computed): long prompts are cut into chunks that run between
+// decode steps ("vLLM推理引擎PagedAttention原理与性能优化实战", §六). A chunk of n new
+// tokens is the last n positions of its sequence's context; their K/V are already in the
+// paged cache, and new token i attends causally to positions 0 .. ctx - n + i through the
+// sequence's block table, with ordinary softmax attention ("vLLM 推理优化技术深度调研报告",
+// 维度一.3 公式 3-4). Prefill is the compute-bound phase (same page, 公式 5), so here the
+// matrix cores carry the work.
+//
+// How it is computed here (this design is not from the pages):
+// * rows of one (sequence, kv head) are its new tokens x the G query heads of the group,
+//   token-major; a workgroup of 4 wavefronts takes 128 consecutive rows, 32 per wavefront
+//   as two 16-column MFMA blocks, so the K/V tiles it stages in LDS serve every query
+//   head of the group;
+// * keys are taken 64 at a time (four cache blocks): the workgroup loads the next tile
+//   into registers (16-byte loads, each instruction covering one contiguous KiB of a
+//   block) while computing on the current one, then stores it to the other half of a
+//   double-buffered LDS area as XOR-swizzled 16-byte chunks; one barrier per tile;
+// * S^T[16 keys x 16 rows] = K . Q^T on v_mfma_f32_16x16x32 with Q^T held in registers;
+//   O^T[16 d x 16 rows] += V^T . P^T on v_mfma_f32_16x16x32 over 32 keys, with V^T read by
+//   ds_read_b64_tr_b16. The contraction runs over keys (4j4..4j4+3 of one 16-key tile,
+//   then the same of the next), the order in which the score accumulators already hold P,
+//   so softmax weights never leave their lanes;
+// * online softmax in fp32 with exp2 (log2 e folded into the scale); the causal limit of
+//   each row is applied by select only on tiles that reach past the wavefront's first
+//   row's limit; a wavefront skips tiles wholly past its last row;
+// * V rows past the workgroup's last key are zeroed when staged (0 * stale NaN would
+//   poison the product); an fp8 (OCP E4M3FN) cache is widened exactly to the q dtype as
+//   it is staged, its per-tensor scales folded into the logit and output scales;
+// * work items are ordered kv head, sequence, row tile (last rows first: they see the
+//   most keys), and each XCD takes a contiguous range of them, so the row tiles of one
+//   (sequence, kv head) run on one XCD and re-read its K/V from that XCD's L2.
+#include "pkv_launch.h"
+
+namespace pkv {
+
+template <int QT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (QT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <int KVT, int D>
+struct PrefillTraits {
+  static constexpr int kThreads = kWave * kPrefillWaves;
+  static constexpr int kElem = (KVT == kFP8) ? 1 : 2;              // bytes per cache element
+  static constexpr int kBlockBytes = kBlock * D * kElem;           // one kv head's slice of a block
+  static constexpr int kChunksPerBlock = kBlockBytes / 16;
+  static constexpr int kLoads = kPrefillKeys * D * kElem / 16 / kThreads;  // per thread, K (or V)
+  static constexpr int kRowChunks = D / 8;                         // 16-byte chunks per LDS row
+  static constexpr int kTileLds = kPrefillKeys * D * 2;            // one K or V tile in LDS
+  static_assert(kChunksPerBlock % kWave == 0, "a wavefront's loads stay inside one block");
+  static_assert(kLoads >= 1, "every thread loads");
+};
+
+template <int QT, int KVT, int D>
+__global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(const PrefillArgs a) {
+  using Tr = PrefillTraits<KVT, D>;
+  constexpr int RC = Tr::kRowChunks;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][Tr::kTileLds];   // [buffer][K, V]
+
+  // ---- work item ----------------------------------------------------------------------
+  const int nb = gridDim.x;                       // a multiple of 8
+  const int item = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+  if (item >= a.num_items) return;
+  const int pair = item / a.row_tiles;
+  const int tile = a.row_tiles - 1 - item % a.row_tiles;
+  const int g = pair / a.num_seqs, s = pair % a.num_seqs;
+  const int G = a.group;
+
+  const int ctx = min(max(a.context_lens[s], 0), a.max_blocks * kBlock);
+  const int q0 = a.query_start_loc[s], q1 = a.query_start_loc[s + 1];
+  if (q0 < 0 || q1 < q0 || q1 > a.num_tokens) return;
+  const int n = min(min(q1 - q0, a.max_query_len), ctx);
+  const int R = n * G;
+  const int row0 = tile * kPrefillRows;
+  if (row0 >= R) return;
+  const int prefix = ctx - n;
+  const int kv_end = prefix + (min(R, row0 + kPrefillRows) - 1) / G + 1;   // keys the workgroup needs
+  const int nblk = (kv_end + kBlock - 1) / kBlock;
+  const int n_iter = (kv_end + kPrefillKeys - 1) / kPrefillKeys;
+
+  const int t = threadIdx.x, w = readfirstlane(t / kWave), lane = t & (kWave - 1);
+  const int n16 = lane & 15, j4 = lane >> 4;
+
+  // ---- this wavefront's rows: Q^T operands and causal limits ------------------------------
+  const int wrow0 = row0 + w * kPrefillCols;
+  u32x4 qb[2][D / 32];
+  int limit[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = wrow0 + cb * 16 + n16;
+    const bool valid = r < R;
+    const int tok = valid ? r / G : 0, h = valid ? r % G : 0;
+    limit[cb] = valid ? prefix + tok + 1 : 0;
+    const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)(q0 + tok) * a.q_token_stride + (int64_t)(g * G + h) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+      qb[cb][c] = valid ? *(const u32x4*)(qrow + 32 * c + 8 * j4) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const bool wave_live = wrow0 < R;
+  const int wave_lo = wave_live ? prefix + wrow0 / G + 1 : 0;                      // first row's limit
+  const int wave_hi = wave_live ? prefix + (min(R, wrow0 + kPrefillCols) - 1) / G + 1 : 0;   // last row's
+
+  // ---- K/V tiles: global -> registers -> LDS ----------------------------------------------
+  const int64_t head_stride = Tr::kBlockBytes;
+  const int64_t block_stride = (int64_t)a.num_kv_heads * head_stride;
+  const uint8_t* kbase = (const uint8_t*)a.k_cache + (int64_t)g * head_stride;
+  const uint8_t* vbase = (const uint8_t*)a.v_cache + (int64_t)g * head_stride;
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
+
+  u32x4 rk[Tr::kLoads], rv[Tr::kLoads];
+  // Load u of thread t covers 16-byte chunk f = u * threads + t of the tile; its block
+  // (0..3) is the same for the whole wavefront.
+  auto load_tile = [&](int i) {
+#pragma unroll
+    for (int u = 0; u < Tr::kLoads; ++u) {
+      const int j = (u * Tr::kThreads + w * kWave) / Tr::kChunksPerBlock;
+      const int blk = i * (kPrefillKeys / kBlock) + j;
+      int id = blk < nblk ? bt[blk] : -1;
+      id = readfirstlane(id);
+      const bool live = id >= 0 && id < a.num_blocks;
+      const int64_t off = (live ? (int64_t)id : 0) * block_stride;
+      const uint32_t bytes = live ? (uint32_t)Tr::kBlockBytes : 0u;   // 0: loads return zeros
+      const uint32_t c16 = (uint32_t)((u * Tr::kThreads + t) % Tr::kChunksPerBlock) * 16;
+      rk[u] = buf_load16<kPolicyCached>(make_rsrc(kbase + off, bytes), c16);
+      rv[u] = buf_load16<kPolicyCached>(make_rsrc(vbase + off, bytes), c16);
+    }
+  };
+  // LDS row r of a tile holds key r of the tile as 16-bit values; its chunk k is stored at
+  // position k ^ (r mod RC). V rows at or past kv_end are stored as zeros.
+  auto stage_tile = [&](int i, int buf) {
+    uint8_t* kl = lds[buf][0];
+    uint8_t* vl = lds[buf][1];
+#pragma unroll
+    for (int u = 0; u < Tr::kLoads; ++u) {
+      const int f = u * Tr::kThreads + t;
+      const int j = f / Tr::kChunksPerBlock, c = f % Tr::kChunksPerBlock;
+      if constexpr (KVT == kFP8) {
+        const int r = j * kBlock + c / (D / 16), ch = c % (D / 16);
+        const u32x4 wk = rk[u];
+        const u32x4 wv = i * kPrefillKeys + r < kv_end ? rv[u] : u32x4{0u, 0u, 0u, 0u};
+        const int sw = r & (RC - 1);
+        const u32x2 k0 = fp8x4_to_16<QT>(wk[0]), k1 = fp8x4_to_16<QT>(wk[1]);
+        const u32x2 k2 = fp8x4_to_16<QT>(wk[2]), k3 = fp8x4_to_16<QT>(wk[3]);
+        const u32x2 v0 = fp8x4_to_16<QT>(wv[0]), v1 = fp8x4_to_16<QT>(wv[1]);
+        const u32x2 v2 = fp8x4_to_16<QT>(wv[2]), v3 = fp8x4_to_16<QT>(wv[3]);
+        const int o0 = (r * RC + ((2 * ch) ^ sw)) * 16, o1 = (r * RC + ((2 * ch + 1) ^ sw)) * 16;
+        *(u32x4*)(kl + o0) = u32x4{k0[0], k0[1], k1[0], k1[1]};
+        *(u32x4*)(kl + o1) = u32x4{k2[0], k2[1], k3[0], k3[1]};
+        *(u32x4*)(vl + o0) = u32x4{v0[0], v0[1], v1[0], v1[1]};
+        *(u32x4*)(vl + o1) = u32x4{v2[0], v2[1], v3[0], v3[1]};
+      } else {
+        const int r = j * kBlock + c / RC, ch = c % RC;
+        const int o = (r * RC + (ch ^ (r & (RC - 1)))) * 16;
+        *(u32x4*)(kl + o) = rk[u];
+        *(u32x4*)(vl + o) = i * kPrefillKeys + r < kv_end ? rv[u] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  // ---- running softmax state: per lane, column n16 of each block, rows 4j4.. of each d-tile
+  f32x4 o[2][D / 16];
+  float m[2], l[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) o[cb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[cb] = -INFINITY;
+    l[cb] = 0.f;
+  }
+  const float qk_scale = a.qk_scale_log2;
+
+  auto compute = [&](int i, int buf) {
+    const uint8_t* kl = lds[buf][0];
+    const uint8_t* vl = lds[buf][1];
+    const int k0 = i * kPrefillKeys;
+    // S^T = K . Q^T for the four 16-key tiles.
+    f32x4 sc[4][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      sc[kt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sc[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = kt * 16 + n16;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        const int ch = 4 * c + j4;                        // elements 32c + 8j4 .. + 7
+        const u32x4 ka = *(const u32x4*)(kl + (r * RC + (ch ^ (r & (RC - 1)))) * 16);
+        sc[kt][0] = mfma16x16x32<QT>(ka, qb[0][c], sc[kt][0]);
+        sc[kt][1] = mfma16x16x32<QT>(ka, qb[1][c], sc[kt][1]);
+      }
+    }
+    // Causal limits (and keys past the workgroup's last one) on tiles that reach them.
+    if (k0 + kPrefillKeys > wave_lo) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (k0 + kt * 16 + 4 * j4 + e >= limit[cb]) sc[kt][cb][e] = -INFINITY;
+    }
+    // Online softmax per column block; P^T packed as the B operands of the PV steps.
+    u32x4 pb[2][2];   // [32-key half][column block]
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        mx = fmaxf(mx, fmaxf(fmaxf(sc[kt][cb][0], sc[kt][cb][1]), fmaxf(sc[kt][cb][2], sc[kt][cb][3])));
+      mx = max_xor32(max_xor16(mx));
+      const float m_new = fmaxf(m[cb], mx * qk_scale);     // the scale is positive
+      // A column that has seen no live key keeps m = -inf; exponents are then taken
+      // against 0 so that they come out as exp2(-inf) = 0, never as exp2(-inf + inf).
+      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = m[cb] == m_new ? 1.0f : exp2_fast(m[cb] - m_ref);
+      m[cb] = m_new;
+      float psum = 0.f;
+      uint32_t pk[4][2];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const float e0 = exp2_fast(fmaf(sc[kt][cb][0], qk_scale, -m_ref));
+        const float e1 = exp2_fast(fmaf(sc[kt][cb][1], qk_scale, -m_ref));
+        const float e2 = exp2_fast(fmaf(sc[kt][cb][2], qk_scale, -m_ref));
+        const float e3 = exp2_fast(fmaf(sc[kt][cb][3], qk_scale, -m_ref));
+        psum += (e0 + e1) + (e2 + e3);
+        pk[kt][0] = pack2<QT>(e0, e1);
+        pk[kt][1] = pack2<QT>(e2, e3);
+      }
+      l[cb] = l[cb] * alpha + psum;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) o[cb][c] *= alpha;
+      }
+      pb[0][cb] = u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+      pb[1][cb] = u32x4{pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
+    }
+    // O^T += V^T . P^T, 32 keys per step.
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int ra = hf * 32 + 4 * j4 + (n16 >> 2), rb = ra + 16;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const int ch = 2 * c + ((n16 & 3) >> 1);
+        const int byte = (n16 & 1) * 8;
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vl + (ra * RC + (ch ^ (ra & (RC - 1)))) * 16 + byte));
+        const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vl + (rb * RC + (ch ^ (rb & (RC - 1)))) * 16 + byte));
+        const u32x2 wa = __builtin_bit_cast(u32x2, va), wb = __builtin_bit_cast(u32x2, vb);
+        const u32x4 av = {wa[0], wa[1], wb[0], wb[1]};
+        o[0][c] = mfma16x16x32<QT>(av, pb[hf][0], o[0][c]);
+        o[1][c] = mfma16x16x32<QT>(av, pb[hf][1], o[1][c]);
+      }
+    }
+  };
+
+  // ---- main loop: one tile in LDS, the next in flight ----------------------------------
+  load_tile(0);
+  stage_tile(0, 0);
+  __syncthreads();
+  for (int i = 0; i < n_iter; ++i) {
+    const bool more = i + 1 < n_iter;
+    if (more) load_tile(i + 1);
+    if (i * kPrefillKeys < wave_hi) compute(i, i & 1);
+    if (more) stage_tile(i + 1, (i + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- results ----------------------------------------------------------------------------
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float l_tot = sum_xor32(sum_xor16(l[cb]));
+    const int r = wrow0 + cb * 16 + n16;
+    if (r < R) {
+      const int tok = r / G, h = r % G;
+      const float inv = a.v_scale / l_tot;
+      uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + tok) * a.num_q_heads + g * G + h) * D;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const f32x4 v = o[cb][c] * inv;
+        *(u32x2*)(orow + 16 * c + 4 * j4) = u32x2{pack2<QT>(v[0], v[1]), pack2<QT>(v[2], v[3])};
+      }
+    }
+  }
+}
+
+template <int QT, int KVT, int D>
+static hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
+  const int grid = (a.num_items + 7) / 8 * 8;
+  hipLaunchKernelGGL((paged_prefill_mfma<QT, KVT, D>), dim3(grid), dim3(kWave * kPrefillWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int q_type, int kv_type, int head_dim, hipStream_t stream) {
+#define PKV_CASE(QT, KVT, D) \
+  if (q_type == QT && kv_type == KVT && head_dim == D) return launch_t<QT, KVT, D>(a, stream);
+  PKV_CASE(kBF16, kBF16, 128) PKV_CASE(kBF16, kBF16, 64)
+  PKV_CASE(kF16, kF16, 128) PKV_CASE(kF16, kF16, 64)
+  PKV_CASE(kBF16, kFP8, 128) PKV_CASE(kBF16, kFP8, 64)
+  PKV_CASE(kF16, kFP8, 128) PKV_CASE(kF16, kFP8, 64)
+#undef PKV_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

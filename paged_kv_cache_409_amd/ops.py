@@ -127,6 +127,32 @@ def decode_step(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables
     return out
 
 
+def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float,
+                            max_query_len: int, k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+    """Causal attention of each sequence's chunk of new tokens (rows query_start_loc[s] ..
+    query_start_loc[s+1] of q) over its paged context (see pkv_paged_attention_prefill)."""
+    _dev(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc)
+    T, Hq, D = q.shape
+    NB, Hkv, P, D2 = k_cache.shape
+    S = context_lens.shape[0]
+    if tuple(out.shape) != (T, Hq, D) or tuple(v_cache.shape) != tuple(k_cache.shape) or D2 != D:
+        raise ValueError("shape mismatch")
+    if out.dtype != q.dtype or v_cache.dtype != k_cache.dtype:
+        raise ValueError("dtype mismatch")
+    for name, t in (("block_tables", block_tables), ("context_lens", context_lens),
+                    ("query_start_loc", query_start_loc)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start_loc.shape != (S + 1,):
+        raise ValueError("block_tables / query_start_loc shape mismatch")
+    st = _lib.load().pkv_paged_attention_prefill(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), query_start_loc.data_ptr(), S, T, Hq, Hkv, D, P, NB, block_tables.shape[1],
+        max_query_len, _dtype(q), _dtype(k_cache), scale, k_scale, v_scale, 0, _stream(stream))
+    _check("pkv_paged_attention_prefill", st)
+    return out
+
+
 def reshape_and_cache(key, value, slot_mapping, k_cache, v_cache, k_scale: float = 1.0, v_scale: float = 1.0,
                       stream=None) -> None:
     """Write key/value [T, Hkv, D] rows into their slots of one layer's caches."""

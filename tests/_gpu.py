@@ -38,6 +38,7 @@ class HostBatch:
         self.context_lens = b.context_lens.cpu().numpy()
         self.slot_mapping = b.slot_mapping.cpu().numpy()
         self.copy_pairs = b.copy_pairs.cpu().numpy()
+        self.query_start_loc = b.query_start_loc.cpu().numpy()
         self.scale, self.k_scale, self.v_scale = b.scale, b.k_scale, b.v_scale
 
 
@@ -85,7 +86,7 @@ def device_batch(cfg: WorkloadConfig, replica: int = 0):
     """Small configs: draw on the CPU (reproducible everywhere), then move to the GPU."""
     b = make_batch(cfg, "cpu", replica)
     for name in ("q", "new_k", "new_v", "k_cache", "v_cache", "block_tables", "context_lens", "slot_mapping",
-                 "copy_pairs"):
+                 "copy_pairs", "query_start_loc"):
         setattr(b, name, getattr(b, name).cuda())
     return b
 
@@ -108,3 +109,34 @@ def clone_batch(b):
     c.k_cache = b.k_cache.clone()
     c.v_cache = b.v_cache.clone()
     return c
+
+
+def oracle_prefill(h: HostBatch, k_cache, v_cache, seqs=None, context_lens=None, query_start_loc=None):
+    ctx = h.context_lens if context_lens is None else context_lens
+    qsl = h.query_start_loc if query_start_loc is None else query_start_loc
+    return attention.paged_prefill_attention(h.q, k_cache, v_cache, h.block_tables, ctx, qsl, h.scale,
+                                             h.cfg.dtype, h.cfg.kv_dtype, h.k_scale, h.v_scale, seqs=seqs)
+
+
+def max_query_len(b) -> int:
+    return int((b.query_start_loc[1:] - b.query_start_loc[:-1]).max().item()) if len(b.context_lens) else 0
+
+
+def gpu_prefill(b, out=None, context_lens=None, query_start_loc=None, max_q=None, k_cache=None, v_cache=None):
+    out = torch.empty_like(b.q) if out is None else out
+    pkv.paged_attention_prefill(out, b.q, b.k_cache if k_cache is None else k_cache,
+                                b.v_cache if v_cache is None else v_cache, b.block_tables,
+                                b.context_lens if context_lens is None else context_lens,
+                                b.query_start_loc if query_start_loc is None else query_start_loc,
+                                b.scale, max_query_len(b) if max_q is None else max_q, b.k_scale, b.v_scale)
+    return out
+
+
+def gpu_prefill_step(b, out=None):
+    """A prefill chunk: the cache write of its new tokens, then causal attention over the cache."""
+    pkv.reshape_and_cache(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale, b.v_scale)
+    return gpu_prefill(b, out)
+
+
+def rows_of(h: HostBatch, seqs):
+    return np.concatenate([np.arange(h.query_start_loc[s], h.query_start_loc[s + 1]) for s in seqs])

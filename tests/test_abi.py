@@ -115,3 +115,30 @@ def test_fused_step_argument_errors():
     assert step(kstride=260) == -6             # not a multiple of 8 elements
     assert step(Hq=7) == -2
     assert step(S=0) == 0
+
+
+def test_prefill_argument_errors_are_reported_before_any_launch():
+    lib = _lib.load()
+
+    def pf(**kw):
+        a = dict(out=16, q=16, qsl=16, S=4, T=64, Hq=8, Hkv=2, D=128, P=16, maxb=8, maxq=32,
+                 qt=_lib.PKV_BF16, kt=_lib.PKV_BF16, scale=0.1, ks=1.0, vs=1.0, qstride=0)
+        a.update(kw)
+        return lib.pkv_paged_attention_prefill(a["out"], a["q"], 16, 16, 16, 16, a["qsl"], a["S"], a["T"], a["Hq"],
+                                               a["Hkv"], a["D"], a["P"], 64, a["maxb"], a["maxq"], a["qt"], a["kt"],
+                                               a["scale"], a["ks"], a["vs"], a["qstride"], None)
+    assert pf(qsl=None) == -1
+    assert pf(out=None) == -1
+    assert pf(Hq=7) == -2                           # not a multiple of Hkv
+    assert pf(scale=0.0) == -2                      # the logit scale must be positive
+    assert pf(scale=float("nan")) == -2
+    assert pf(maxq=-1) == -2
+    assert pf(qstride=100) == -2                    # shorter than one token's query row
+    assert pf(qt=_lib.PKV_FP8_E4M3) == -3
+    assert pf(kt=_lib.PKV_F16) == -3
+    assert pf(D=96) == -4
+    assert pf(P=64) == -4
+    assert pf(kt=_lib.PKV_FP8_E4M3, vs=0.0) == -2
+    assert pf(q=8) == -6                            # misaligned
+    assert pf(qstride=1028) == -6                   # not a multiple of 8 elements
+    assert pf(S=0) == 0 and pf(T=0) == 0 and pf(maxq=0) == 0    # nothing to do
