@@ -45,6 +45,36 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// acc + lo + hi of two packed 16-bit values (one v_dot2 against (1, 1)).
+template <int QT>
+__device__ __forceinline__ float dot2_ones(uint32_t p, float acc) {
+  if constexpr (QT == kBF16) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
+  } else {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), one, acc, false);
+  }
+}
+
+constexpr float kLazyRescale = 8.0f;
+constexpr int kIdsRing = 1024;   // block-table entries a workgroup keeps in LDS
+
+// Maxima of scores. This file is compiled with -fno-honor-nans: no score that reaches a
+// maximum or an exponent is NaN (stale rows are replaced by -inf through a select on an
+// integer condition first), so IEEE max needs no NaN-quieting of operands that come
+// straight from the matrix cores, and chains of maxima become v_max3.
+__device__ __forceinline__ float max_nn(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ float max3_nn(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+__device__ __forceinline__ float max_nn_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_nn_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int KVT, int D>
 struct PrefillTraits {
   static constexpr int kThreads = kWave * kPrefillWaves;
@@ -52,8 +82,14 @@ struct PrefillTraits {
   static constexpr int kBlockBytes = kBlock * D * kElem;           // one kv head's slice of a block
   static constexpr int kChunksPerBlock = kBlockBytes / 16;
   static constexpr int kLoads = kPrefillKeys * D * kElem / 16 / kThreads;  // per thread, K (or V)
-  static constexpr int kRowChunks = D / 8;                         // 16-byte chunks per LDS row
-  static constexpr int kTileLds = kPrefillKeys * D * 2;            // one K or V tile in LDS
+  // LDS rows are padded rather than swizzled, so that every operand read is a per-lane
+  // base plus an immediate offset. K rows (read 16 bytes per lane, 8 rows per bank
+  // cycle) step 4 banks; V rows (read transposed, 4 rows x 32 bytes per bank cycle) step
+  // 8 banks.
+  static constexpr int kKRow = D * 2 + 16;
+  static constexpr int kVRow = D * 2 + 32;
+  static constexpr int kKTile = kPrefillKeys * kKRow;
+  static constexpr int kVTile = kPrefillKeys * kVRow;
   static_assert(kChunksPerBlock % kWave == 0, "a wavefront's loads stay inside one block");
   static_assert(kLoads >= 1, "every thread loads");
 };
@@ -61,8 +97,8 @@ struct PrefillTraits {
 template <int QT, int KVT, int D>
 __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(const PrefillArgs a) {
   using Tr = PrefillTraits<KVT, D>;
-  constexpr int RC = Tr::kRowChunks;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][Tr::kTileLds];   // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][Tr::kKTile + Tr::kVTile];   // [buffer]: K tile, V tile
+  __shared__ __attribute__((aligned(16))) int ids_lds[kIdsRing];
 
   // ---- work item ----------------------------------------------------------------------
   const int nb = gridDim.x;                       // a multiple of 8
@@ -86,6 +122,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
   const int n_iter = (kv_end + kPrefillKeys - 1) / kPrefillKeys;
 
   const int t = threadIdx.x, w = readfirstlane(t / kWave), lane = t & (kWave - 1);
+  __builtin_assume(w >= 0 && w < kPrefillWaves);
   const int n16 = lane & 15, j4 = lane >> 4;
 
   // ---- this wavefront's rows: Q^T operands and causal limits ------------------------------
@@ -113,18 +150,33 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
   const uint8_t* kbase = (const uint8_t*)a.k_cache + (int64_t)g * head_stride;
   const uint8_t* vbase = (const uint8_t*)a.v_cache + (int64_t)g * head_stride;
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
+  const int num_blocks = (int)min(a.num_blocks, (int64_t)0x7fffffff);
 
-  u32x4 rk[Tr::kLoads], rv[Tr::kLoads];
+  // Block ids are staged in an LDS ring of kIdsRing table entries (-1 past the last
+  // block), refilled by the whole workgroup when the tiles reach its end. A tile's four
+  // ids are read from the ring one iteration before its loads are issued.
+  auto fill_ids = [&](int first) {   // entries [first, first + kIdsRing); first is a multiple of kIdsRing
+    for (int k = t; k < kIdsRing; k += Tr::kThreads) ids_lds[k] = first + k < nblk ? bt[first + k] : -1;
+  };
+  auto read_ids = [&](int i) -> u32x4 {   // ids of tile i's four blocks (same address in every lane)
+    return *(const u32x4*)(ids_lds + ((i * (kPrefillKeys / kBlock)) & (kIdsRing - 1)));
+  };
+
+  // Two register sets: even tiles in A, odd tiles in B. Tile i + 2 is loaded while tile i
+  // is multiplied and tile i + 1 is staged, so a load has two tiles' time to arrive.
+  // Loads are issued for every tile, past the last one too (as zero-length loads), so that
+  // the count of loads in flight is the same on every path.
+  u32x4 rk_a[Tr::kLoads], rv_a[Tr::kLoads], rk_b[Tr::kLoads], rv_b[Tr::kLoads];
   // Load u of thread t covers 16-byte chunk f = u * threads + t of the tile; its block
   // (0..3) is the same for the whole wavefront.
-  auto load_tile = [&](int i) {
+  auto load_tile = [&](const u32x4 ids, u32x4* rk, u32x4* rv) {
+    const int id0 = readfirstlane((int)ids[0]), id1 = readfirstlane((int)ids[1]);
+    const int id2 = readfirstlane((int)ids[2]), id3 = readfirstlane((int)ids[3]);
 #pragma unroll
     for (int u = 0; u < Tr::kLoads; ++u) {
       const int j = (u * Tr::kThreads + w * kWave) / Tr::kChunksPerBlock;
-      const int blk = i * (kPrefillKeys / kBlock) + j;
-      int id = blk < nblk ? bt[blk] : -1;
-      id = readfirstlane(id);
-      const bool live = id >= 0 && id < a.num_blocks;
+      const int id = j == 0 ? id0 : j == 1 ? id1 : j == 2 ? id2 : id3;
+      const bool live = id >= 0 && id < num_blocks;
       const int64_t off = (live ? (int64_t)id : 0) * block_stride;
       const uint32_t bytes = live ? (uint32_t)Tr::kBlockBytes : 0u;   // 0: loads return zeros
       const uint32_t c16 = (uint32_t)((u * Tr::kThreads + t) % Tr::kChunksPerBlock) * 16;
@@ -132,34 +184,33 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
       rv[u] = buf_load16<kPolicyCached>(make_rsrc(vbase + off, bytes), c16);
     }
   };
-  // LDS row r of a tile holds key r of the tile as 16-bit values; its chunk k is stored at
-  // position k ^ (r mod RC). V rows at or past kv_end are stored as zeros.
-  auto stage_tile = [&](int i, int buf) {
-    uint8_t* kl = lds[buf][0];
-    uint8_t* vl = lds[buf][1];
+  // LDS row r of a tile holds key r of the tile as 16-bit values. V rows at or past
+  // kv_end are stored as zeros.
+  auto stage_tile = [&](int i, int buf, const u32x4* rk, const u32x4* rv) {
+    uint8_t* kl = lds[buf];
+    uint8_t* vl = lds[buf] + Tr::kKTile;
 #pragma unroll
     for (int u = 0; u < Tr::kLoads; ++u) {
       const int f = u * Tr::kThreads + t;
       const int j = f / Tr::kChunksPerBlock, c = f % Tr::kChunksPerBlock;
       if constexpr (KVT == kFP8) {
-        const int r = j * kBlock + c / (D / 16), ch = c % (D / 16);
+        const int r = j * kBlock + c / (D / 16), ch = c % (D / 16);   // 16 codes = 2 LDS chunks
         const u32x4 wk = rk[u];
         const u32x4 wv = i * kPrefillKeys + r < kv_end ? rv[u] : u32x4{0u, 0u, 0u, 0u};
-        const int sw = r & (RC - 1);
         const u32x2 k0 = fp8x4_to_16<QT>(wk[0]), k1 = fp8x4_to_16<QT>(wk[1]);
         const u32x2 k2 = fp8x4_to_16<QT>(wk[2]), k3 = fp8x4_to_16<QT>(wk[3]);
         const u32x2 v0 = fp8x4_to_16<QT>(wv[0]), v1 = fp8x4_to_16<QT>(wv[1]);
         const u32x2 v2 = fp8x4_to_16<QT>(wv[2]), v3 = fp8x4_to_16<QT>(wv[3]);
-        const int o0 = (r * RC + ((2 * ch) ^ sw)) * 16, o1 = (r * RC + ((2 * ch + 1) ^ sw)) * 16;
-        *(u32x4*)(kl + o0) = u32x4{k0[0], k0[1], k1[0], k1[1]};
-        *(u32x4*)(kl + o1) = u32x4{k2[0], k2[1], k3[0], k3[1]};
-        *(u32x4*)(vl + o0) = u32x4{v0[0], v0[1], v1[0], v1[1]};
-        *(u32x4*)(vl + o1) = u32x4{v2[0], v2[1], v3[0], v3[1]};
+        uint8_t* kd = kl + r * Tr::kKRow + ch * 32;
+        uint8_t* vd = vl + r * Tr::kVRow + ch * 32;
+        *(u32x4*)(kd) = u32x4{k0[0], k0[1], k1[0], k1[1]};
+        *(u32x4*)(kd + 16) = u32x4{k2[0], k2[1], k3[0], k3[1]};
+        *(u32x4*)(vd) = u32x4{v0[0], v0[1], v1[0], v1[1]};
+        *(u32x4*)(vd + 16) = u32x4{v2[0], v2[1], v3[0], v3[1]};
       } else {
-        const int r = j * kBlock + c / RC, ch = c % RC;
-        const int o = (r * RC + (ch ^ (r & (RC - 1)))) * 16;
-        *(u32x4*)(kl + o) = rk[u];
-        *(u32x4*)(vl + o) = i * kPrefillKeys + r < kv_end ? rv[u] : u32x4{0u, 0u, 0u, 0u};
+        const int r = j * kBlock + c / (D / 8), ch = c % (D / 8);
+        *(u32x4*)(kl + r * Tr::kKRow + ch * 16) = rk[u];
+        *(u32x4*)(vl + r * Tr::kVRow + ch * 16) = i * kPrefillKeys + r < kv_end ? rv[u] : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -176,9 +227,14 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
   }
   const float qk_scale = a.qk_scale_log2;
 
+  // Per-lane LDS bases: K fragment (row n16, elements 8j4..), V^T fragment (rows 4j4 +
+  // n16/4, elements 4 (n16 & 3)..).
+  const int k_lane = n16 * Tr::kKRow + j4 * 16;
+  const int v_lane = (4 * j4 + (n16 >> 2)) * Tr::kVRow + (n16 & 3) * 8;
+
   auto compute = [&](int i, int buf) {
-    const uint8_t* kl = lds[buf][0];
-    const uint8_t* vl = lds[buf][1];
+    const uint8_t* kl = lds[buf] + k_lane;
+    const uint8_t* vl = lds[buf] + Tr::kKTile + v_lane;
     const int k0 = i * kPrefillKeys;
     // S^T = K . Q^T for the four 16-key tiles.
     f32x4 sc[4][2];
@@ -186,11 +242,9 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
     for (int kt = 0; kt < 4; ++kt) {
       sc[kt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       sc[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int r = kt * 16 + n16;
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
-        const int ch = 4 * c + j4;                        // elements 32c + 8j4 .. + 7
-        const u32x4 ka = *(const u32x4*)(kl + (r * RC + (ch ^ (r & (RC - 1)))) * 16);
+        const u32x4 ka = *(const u32x4*)(kl + kt * 16 * Tr::kKRow + c * 64);   // elements 32c + 8j4 .. + 7
         sc[kt][0] = mfma16x16x32<QT>(ka, qb[0][c], sc[kt][0]);
         sc[kt][1] = mfma16x16x32<QT>(ka, qb[1][c], sc[kt][1]);
       }
@@ -209,49 +263,51 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
     u32x4 pb[2][2];   // [32-key half][column block]
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        mx = fmaxf(mx, fmaxf(fmaxf(sc[kt][cb][0], sc[kt][cb][1]), fmaxf(sc[kt][cb][2], sc[kt][cb][3])));
-      mx = max_xor32(max_xor16(mx));
-      const float m_new = fmaxf(m[cb], mx * qk_scale);     // the scale is positive
+      // (scores are never NaN here: stale rows were replaced by -inf above)
+      const float m0 = max3_nn(sc[0][cb][0], sc[0][cb][1], sc[0][cb][2]);
+      const float m1 = max3_nn(sc[0][cb][3], sc[1][cb][0], sc[1][cb][1]);
+      const float m2 = max3_nn(sc[1][cb][2], sc[1][cb][3], sc[2][cb][0]);
+      const float m3 = max3_nn(sc[2][cb][1], sc[2][cb][2], sc[2][cb][3]);
+      const float m4 = max3_nn(sc[3][cb][0], sc[3][cb][1], sc[3][cb][2]);
+      float mx = max_nn(max3_nn(m0, m1, m2), max3_nn(m3, m4, sc[3][cb][3]));
+      mx = max_nn_xor32(max_nn_xor16(mx)) * qk_scale;    // the scale is positive
+      // Lazy rescaling: the reference point m of a column moves only when a score
+      // exceeds it by more than kLazyRescale (log2 units), so weights stay below 2^8 and
+      // the accumulators are rescaled rarely. Any reference gives the same quotient.
+      const float m_new = mx > m[cb] + kLazyRescale ? mx : m[cb];
+      const float alpha = m[cb] == m_new ? 1.0f : exp2_fast(m[cb] - m_new);   // exp2(-inf) = 0
+      m[cb] = m_new;
       // A column that has seen no live key keeps m = -inf; exponents are then taken
       // against 0 so that they come out as exp2(-inf) = 0, never as exp2(-inf + inf).
       const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = m[cb] == m_new ? 1.0f : exp2_fast(m[cb] - m_ref);
-      m[cb] = m_new;
-      float psum = 0.f;
       uint32_t pk[4][2];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const float e0 = exp2_fast(fmaf(sc[kt][cb][0], qk_scale, -m_ref));
-        const float e1 = exp2_fast(fmaf(sc[kt][cb][1], qk_scale, -m_ref));
-        const float e2 = exp2_fast(fmaf(sc[kt][cb][2], qk_scale, -m_ref));
-        const float e3 = exp2_fast(fmaf(sc[kt][cb][3], qk_scale, -m_ref));
-        psum += (e0 + e1) + (e2 + e3);
-        pk[kt][0] = pack2<QT>(e0, e1);
-        pk[kt][1] = pack2<QT>(e2, e3);
+        pk[kt][0] = pack2<QT>(exp2_fast(fmaf(sc[kt][cb][0], qk_scale, -m_ref)),
+                              exp2_fast(fmaf(sc[kt][cb][1], qk_scale, -m_ref)));
+        pk[kt][1] = pack2<QT>(exp2_fast(fmaf(sc[kt][cb][2], qk_scale, -m_ref)),
+                              exp2_fast(fmaf(sc[kt][cb][3], qk_scale, -m_ref)));
       }
-      l[cb] = l[cb] * alpha + psum;
       if (__any(alpha != 1.0f)) {
+        l[cb] *= alpha;
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) o[cb][c] *= alpha;
       }
+      // The denominator sums the rounded weights that the PV product uses.
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) l[cb] = dot2_ones<QT>(pk[kt][1], dot2_ones<QT>(pk[kt][0], l[cb]));
       pb[0][cb] = u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
       pb[1][cb] = u32x4{pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
     }
     // O^T += V^T . P^T, 32 keys per step.
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const int ra = hf * 32 + 4 * j4 + (n16 >> 2), rb = ra + 16;
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const int ch = 2 * c + ((n16 & 3) >> 1);
-        const int byte = (n16 & 1) * 8;
-        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vl + (ra * RC + (ch ^ (ra & (RC - 1)))) * 16 + byte));
+        const uint8_t* va_p = vl + hf * 32 * Tr::kVRow + c * 32;
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)va_p);
         const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vl + (rb * RC + (ch ^ (rb & (RC - 1)))) * 16 + byte));
+            (__attribute__((address_space(3))) i16x4*)(va_p + 16 * Tr::kVRow));
         const u32x2 wa = __builtin_bit_cast(u32x2, va), wb = __builtin_bit_cast(u32x2, vb);
         const u32x4 av = {wa[0], wa[1], wb[0], wb[1]};
         o[0][c] = mfma16x16x32<QT>(av, pb[hf][0], o[0][c]);
@@ -260,16 +316,32 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
     }
   };
 
-  // ---- main loop: one tile in LDS, the next in flight ----------------------------------
-  load_tile(0);
-  stage_tile(0, 0);
-  __syncthreads();
-  for (int i = 0; i < n_iter; ++i) {
-    const bool more = i + 1 < n_iter;
-    if (more) load_tile(i + 1);
+  // ---- main loop: one tile in LDS, the next two in flight ------------------------------
+  // ids: the block ids of tile i + 2 on entry; ld: registers that receive tile i + 2;
+  // st: registers that hold tile i + 1.
+  auto iteration = [&](int i, u32x4& ids, u32x4* ld_k, u32x4* ld_v, const u32x4* st_k, const u32x4* st_v) {
+    load_tile(ids, ld_k, ld_v);
     if (i * kPrefillKeys < wave_hi) compute(i, i & 1);
-    if (more) stage_tile(i + 1, (i + 1) & 1);
+    if (((i + 3) * (kPrefillKeys / kBlock)) % kIdsRing == 0) {   // the ring moves on (all waves)
+      fill_ids((i + 3) * (kPrefillKeys / kBlock));
+      __syncthreads();
+    }
+    ids = read_ids(i + 3);
+    if (i + 1 < n_iter) stage_tile(i + 1, (i + 1) & 1, st_k, st_v);
     __syncthreads();
+  };
+  fill_ids(0);
+  __syncthreads();
+  u32x4 ids = read_ids(0);
+  load_tile(ids, rk_a, rv_a);
+  ids = read_ids(1);
+  load_tile(ids, rk_b, rv_b);
+  ids = read_ids(2);
+  stage_tile(0, 0, rk_a, rv_a);
+  __syncthreads();
+  for (int i = 0; i < n_iter; i += 2) {
+    iteration(i, ids, rk_a, rv_a, rk_b, rv_b);
+    if (i + 1 < n_iter) iteration(i + 1, ids, rk_b, rv_b, rk_a, rv_a);
   }
 
   // ---- results ----------------------------------------------------------------------------

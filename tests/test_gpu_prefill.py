@@ -152,3 +152,11 @@ def test_full_size_chunked_prefill_sampled_rows():
     rows = rows_of(h, seqs)
     err = float(np.abs(out.float().cpu().numpy()[rows] - ref[rows]).max())
     assert err <= tol(cfg), f"max abs error {err}"
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_long_contexts_walk_past_the_staged_block_ids(kv_dtype):
+    # Contexts of more than 1024 blocks: the workgroup restages its block ids mid-walk.
+    cfg = prefill_cfg(8, 128, "bf16", kv_dtype, S=3, Hkv=1, ctx=("fixed", [20000, 16400, 16385]),
+                      chunk=("fixed", 40), max_ctx=20000)
+    _case(cfg)
