@@ -1,6 +1,7 @@
-"""Benchmark of one paged decode step on one MI355X.
+"""Benchmark of one paged decode step (or one prefill chunk) on one MI355X.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config llama2_70b_gqa]
+    python bench.py --config prefill_70b_gqa      (a prefill-chunk step, see prefill_bench)
 
 A step is the whole hot path over one synthetic batch: copy-on-write block copies
 (when the batch has any), the cache write of every sequence's new token, then
@@ -31,27 +32,33 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
+PEAK_MFMA_TFLOPS = 2500.0      # MI355X published dense bf16 / fp16 matrix-core rate
 CPU_SAMPLE_SECONDS = 12.0      # target length of the timed oracle sample
 DECODE_SOURCES = ("paged_kv_cache_409_amd/csrc/decode_mfma.hip", "paged_kv_cache_409_amd/csrc/decode_valu.hip",
                   "paged_kv_cache_409_amd/csrc/decode_common.h", "paged_kv_cache_409_amd/csrc/pkv_device.h")
 
 
-def kernel_source_hash() -> str:
+PREFILL_SOURCES = ("paged_kv_cache_409_amd/csrc/prefill_mfma.hip", "paged_kv_cache_409_amd/csrc/decode_common.h",
+                   "paged_kv_cache_409_amd/csrc/pkv_device.h", "paged_kv_cache_409_amd/csrc/pkv_launch.h",
+                   "paged_kv_cache_409_amd/build.py")
+
+
+def kernel_source_hash(sources=DECODE_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(config_name: str, kv_bytes: float):
-    """HBM traffic of one decode launch from committed counter runs, if they match this kernel."""
-    path = os.path.join(ROOT, "profiles", f"decode_traffic_{config_name}.json")
+def load_traffic(config_name: str, kind: str = "decode", sources=DECODE_SOURCES):
+    """HBM traffic of one launch from committed counter runs, if they match this kernel's sources."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_traffic_{config_name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -78,13 +85,15 @@ def main() -> int:
     import torch
 
     import paged_kv_cache_409_amd as pkv
-    from workloads import CONFIGS, make_batch
+    from workloads import CONFIGS, PREFILL_CONFIGS, make_batch
     from workloads.gen import kv_bytes_logical, kv_bytes_unique
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         return copy_calibration(args, dev)
+    if args.config in PREFILL_CONFIGS:
+        return prefill_bench(args, PREFILL_CONFIGS[args.config], dev)
     cfg = CONFIGS[args.config]
     batches = [make_batch(cfg, dev, replica=r) for r in range(args.replicas)]
     lay = batches[0].layout
@@ -169,7 +178,7 @@ def main() -> int:
                       "p50": round(float(np.percentile(dec_ms, 50)) * 1e3, 2),
                       "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(cfg.name, kv_alg),
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(cfg.name),
                      "kernel": "paged_decode_mfma" if cfg.group_size > 1 else "paged_decode_valu",
                      "kernel_source_hash": kernel_source_hash()},
         "cpu_baseline": None,
@@ -178,6 +187,138 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(cfg, batches[0], args.cpu_sample_seqs)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def prefill_flops(cfg, lay) -> float:
+    """Algorithmic matrix flops of a prefill chunk: new token i of sequence s attends to
+    ctx_s - n_s + i + 1 keys, each costing 2 D flops for its score and 2 D for its
+    share of the output, per query head."""
+    n = np.diff(lay.query_start_loc).astype(np.int64)
+    prefix = lay.context_lens.astype(np.int64) - n
+    keys = int((n * prefix + n * (n + 1) // 2).sum())
+    return 4.0 * cfg.head_dim * cfg.num_q_heads * keys
+
+
+def prefill_bench(args, cfg, dev) -> int:
+    """One prefill-chunk step: the cache write of every sequence's chunk of new tokens,
+    then causal attention of the chunk over the paged cache. `value` is matrix TFLOP/s of
+    the whole step (algorithmic flops / step time); `roofline` reports the attention
+    kernel alone against the dense bf16/fp16 matrix-core peak."""
+    import torch
+
+    import paged_kv_cache_409_amd as pkv
+    from workloads import make_batch
+
+    batches = [make_batch(cfg, dev, replica=r) for r in range(args.replicas)]
+    lay = batches[0].layout
+    # Replicas draw their own context lengths, so each has its own flop count.
+    flops_r = [prefill_flops(cfg, b.layout) for b in batches]
+    T = int(lay.query_start_loc[-1])
+    max_q = [int(np.diff(b.layout.query_start_loc).max()) for b in batches]
+    outs = [torch.empty_like(b.q) for b in batches]
+
+    def step(i, ev=None):
+        b = batches[i % len(batches)]
+        pkv.reshape_and_cache(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale, b.v_scale)
+        if ev is not None:
+            ev[0].record()
+        pkv.paged_attention_prefill(outs[i % len(batches)], b.q, b.k_cache, b.v_cache, b.block_tables,
+                                    b.context_lens, b.query_start_loc, b.scale, max_q[i % len(batches)],
+                                    b.k_scale, b.v_scale)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    step_flops = sum(flops_r[(args.warmup + i) % len(batches)] for i in range(args.steps)) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    first = args.warmup + args.steps
+    for i in range(args.steps):
+        step(first + i, evs[i])
+    torch.cuda.synchronize()
+    pf_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    pf_avg_ms = float(pf_ms.mean())
+    ev_flops = sum(flops_r[(first + i) % len(batches)] for i in range(args.steps))
+    achieved = ev_flops / (float(pf_ms.sum()) * 1e-3) / 1e12
+    result = {
+        "metric": "paged prefill-chunk attention: achieved matrix TFLOP/s (% of dense bf16 peak) and tokens/s",
+        "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"q {cfg.dtype}, kv {cfg.kv_dtype}; fp32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.description,
+            "num_seqs": cfg.num_seqs, "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": cfg.head_dim, "block_size": cfg.block_size, "new_tokens": T, "max_query_len": max(max_q),
+            "context_lens_replica0": lay.context_lens.tolist(),
+            "flops_algorithmic_per_replica": flops_r, "flops_algorithmic_mean": round(step_flops),
+            "replicas": args.replicas, "parallelism": "single GPU",
+            "step": "reshape_and_cache (chunk) + paged_attention_prefill",
+        },
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "prefill_us": {"mean": round(pf_avg_ms * 1e3, 2), "p10": round(float(np.percentile(pf_ms, 10)) * 1e3, 2),
+                       "p50": round(float(np.percentile(pf_ms, 50)) * 1e3, 2),
+                       "p90": round(float(np.percentile(pf_ms, 90)) * 1e3, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": load_traffic(cfg.name, "prefill", PREFILL_SOURCES),
+                     "kernel": "paged_prefill_mfma", "kernel_source_hash": kernel_source_hash(PREFILL_SOURCES)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(cfg, batches[0])
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def prefill_cpu_baseline(cfg, b):
+    """Time the float64 prefill oracle, single-threaded, on whole sequences of the batch
+    (as many as fit about CPU_SAMPLE_SECONDS, shortest first)."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention
+
+    def bits(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.element_size() == 2 else t.view(torch.uint8).numpy()
+
+    q, kc, vc = bits(b.q), bits(b.k_cache), bits(b.v_cache)     # the GPU wrote the chunk during timing
+    bt, ctx, qsl = b.block_tables.cpu().numpy(), b.context_lens.cpu().numpy(), b.query_start_loc.cpu().numpy()
+    n = np.diff(qsl).astype(np.int64)
+    work = n * (ctx - n) + n * (n + 1) // 2
+    order = np.argsort(work)
+    run = lambda seqs: attention.paged_prefill_attention(q, kc, vc, bt, ctx, qsl, cfg.scale, cfg.dtype,
+                                                         cfg.kv_dtype, b.k_scale, b.v_scale, seqs=seqs)
+    with threadpool_limits(limits=1):
+        seqs, dt = [], 0.0
+        while dt < CPU_SAMPLE_SECONDS:        # shortest first, cycling over the batch if it is quick
+            s = int(order[len(seqs) % len(order)])
+            t0 = time.perf_counter()
+            run([s])
+            dt += time.perf_counter() - t0
+            seqs.append(s)
+    flops = 4.0 * cfg.head_dim * cfg.num_q_heads * float(work[seqs].sum())
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "tokens_per_s": round(float(n[seqs].sum()) / dt, 2), "cores": 1, "kind": "oracle",
+            "sample": f"{len(seqs)} sequence runs over the {cfg.num_seqs} sequences (all rows and heads, "
+                      f"shortest first), float64 numpy oracle on one host thread, {dt:.1f} s"}
 
 
 def copy_calibration(args, dev) -> int:
