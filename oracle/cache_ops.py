@@ -13,6 +13,11 @@ only the tests, the smoke check and the benchmark's CPU-baseline leg use it.
   fresh block, copies the old contents there and writes the copy
   ("vLLM推理引擎PagedAttention原理与性能优化实战", §3.2). The copy covers the whole
   block, K and V, for every layer's cache.
+* Swapping: under memory pressure whole blocks are moved to CPU memory and back
+  ("vLLM 是什么…", §五 误解三; the scheduler reclaims a preempted request's blocks,
+  "vLLM推理引擎PagedAttention原理与性能优化实战", §四). A swap copies whole blocks, K and V,
+  every layer, from one pool (GPU or host) into another; the block ids on the two sides
+  are independent.
 """
 from __future__ import annotations
 
@@ -58,4 +63,17 @@ def copy_blocks(k_caches, v_caches, src_dst_pairs):
         for layer in range(len(k_out)):
             k_out[layer][dst] = k_caches[layer][src]
             v_out[layer][dst] = v_caches[layer][src]
+    return k_out, v_out
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs):
+    """Return copies of every layer's destination (k, v) pools with dst[layer][d] := src[layer][s]
+    for each pair (s, d). Source and destination are different pools (one on the GPU, one
+    in host memory); their block counts may differ."""
+    k_out = [np.array(k, copy=True) for k in dst_k]
+    v_out = [np.array(v, copy=True) for v in dst_v]
+    for src, dst in np.asarray(src_dst_pairs, dtype=np.int64).reshape(-1, 2):
+        for layer in range(len(k_out)):
+            k_out[layer][dst] = src_k[layer][src]
+            v_out[layer][dst] = src_v[layer][src]
     return k_out, v_out
