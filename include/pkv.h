@@ -9,6 +9,7 @@
  *   pkv_copy_blocks             copy-on-write copies of whole KV blocks
  *   pkv_decode_step             cache write + attention of one decode step, one launch
  *   pkv_paged_attention_prefill causal attention of prefill chunks over the paged cache
+ *   pkv_swap_blocks             move whole blocks between a GPU pool and a pinned host pool
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -247,6 +248,35 @@ int pkv_reshape_and_cache(const void* key, const void* value, const int64_t* slo
 int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers,
                     const int64_t* src_dst_pairs, int num_pairs, int64_t block_bytes, int64_t num_blocks,
                     void* stream);
+
+/*
+ * Swapping blocks between the GPU pool and host memory ("vLLM 是什么…", §五 误解三: when
+ * physical memory runs out, blocks are moved to CPU memory; the scheduler reclaims the
+ * blocks of preempted requests, "vLLM推理引擎PagedAttention原理与性能优化实战", §四). For
+ * every pair (src, dst) and every layer l:
+ *   dst_k_caches[l][dst] = src_k_caches[l][src] and dst_v_caches[l][dst] = src_v_caches[l][src],
+ * whole blocks, byte for byte. Swapping out: the sources are GPU pools and the
+ * destinations host pools; swapping in: the other way round. The copy runs as one kernel
+ * whose loads and stores cross the host link directly, so scattered blocks cost no more
+ * than contiguous ones.
+ *
+ *   src_*_caches / dst_*_caches host arrays of num_layers pointers, each a pool of
+ *                  num_src_blocks / num_dst_blocks blocks of block_bytes bytes. Every pool
+ *                  must be addressable by the GPU: device memory, or host memory allocated
+ *                  pinned through the HIP runtime (hipHostMalloc; torch pin_memory=True),
+ *                  which is mapped for the device at the same address. Memory pinned after
+ *                  the fact by registration is not supported.
+ *   src_dst_pairs  [num_pairs, 2] int64 (src block, dst block), GPU-addressable (device or
+ *                  pinned host memory); a pair with an id out of range is skipped
+ *   block_bytes    bytes of one block of one layer's K (= V) pool; a multiple of 16
+ *
+ * Every dst must be distinct. The source and destination pools are different
+ * allocations (blocks within one pool are copied with pkv_copy_blocks). Host pools are
+ * read or written by the GPU until the stream passes the call. num_pairs = 0 is a no-op.
+ */
+int pkv_swap_blocks(const void* const* src_k_caches, const void* const* src_v_caches, void* const* dst_k_caches,
+                    void* const* dst_v_caches, int num_layers, const int64_t* src_dst_pairs, int num_pairs,
+                    int64_t block_bytes, int64_t num_src_blocks, int64_t num_dst_blocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -48,6 +48,10 @@ SIGNATURES = {
         _c_int, _c_int, _c_int, _c_int, _c_i64,        # num_tokens num_kv_heads head_dim block_size num_blocks
         _c_int, _c_int, _c_f, _c_f,                    # in_dtype kv_dtype k_scale v_scale
         _c_i64, _c_i64, _c_p]),                        # key_stride value_stride stream
+    "pkv_swap_blocks": (_c_int, [
+        ctypes.POINTER(_c_p), ctypes.POINTER(_c_p),           # src_k_caches src_v_caches
+        ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_int,   # dst_k_caches dst_v_caches num_layers
+        _c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_p]),         # pairs num_pairs block_bytes num_src num_dst stream
     "pkv_copy_blocks": (_c_int, [
         ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_int,   # k_caches v_caches num_layers
         _c_p, _c_int, _c_i64, _c_i64, _c_p]),                 # pairs num_pairs block_bytes num_blocks stream

@@ -1,6 +1,7 @@
 // C ABI of libpkv.so: host-side validation and dispatch. Contract in include/pkv.h.
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "pkv.h"
 #include "pkv_launch.h"
@@ -61,6 +62,29 @@ int make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+// The address under which the GPU reaches p: p itself for device memory, the mapped address
+// for host memory pinned through the HIP runtime. Pageable (unregistered) host memory is
+// refused, since a kernel touching it would fault.
+int gpu_address(const void* p, void** out) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();   // clear the runtime's error state
+    return PKV_ERR_UNSUPPORTED;
+  }
+  switch (attr.type) {
+    case hipMemoryTypeHost:
+      if (!attr.devicePointer) return PKV_ERR_UNSUPPORTED;
+      *out = attr.devicePointer;
+      return PKV_OK;
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged:
+      *out = const_cast<void*>(p);
+      return PKV_OK;
+    default:   // unregistered host memory, arrays, anything else
+      return PKV_ERR_UNSUPPORTED;
+  }
+}
 
 }  // namespace
 
@@ -372,8 +396,42 @@ int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers
   }
   const long long chunk_wgs = (block_bytes / 16 + 255) / 256;
   if ((long long)num_pairs * chunk_wgs > (1LL << 31) - 1) return PKV_ERR_SHAPE;
-  return hip_status(pkv::launch_copy_blocks(k_caches, v_caches, num_layers, src_dst_pairs, num_pairs, block_bytes,
-                                            num_blocks, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(pkv::launch_move_blocks(k_caches, v_caches, k_caches, v_caches, num_layers, src_dst_pairs,
+                                            num_pairs, block_bytes, num_blocks, num_blocks,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+int pkv_swap_blocks(const void* const* src_k_caches, const void* const* src_v_caches, void* const* dst_k_caches,
+                    void* const* dst_v_caches, int num_layers, const int64_t* src_dst_pairs, int num_pairs,
+                    int64_t block_bytes, int64_t num_src_blocks, int64_t num_dst_blocks, void* stream) {
+  if (num_layers < 0 || num_pairs < 0 || num_src_blocks <= 0 || num_dst_blocks <= 0 || block_bytes <= 0 ||
+      block_bytes % 16 != 0)
+    return PKV_ERR_SHAPE;
+  if (num_layers == 0 || num_pairs == 0) return PKV_OK;
+  if (!src_k_caches || !src_v_caches || !dst_k_caches || !dst_v_caches || !src_dst_pairs) return PKV_ERR_NULL;
+  for (int l = 0; l < num_layers; ++l) {
+    if (!src_k_caches[l] || !src_v_caches[l] || !dst_k_caches[l] || !dst_v_caches[l]) return PKV_ERR_NULL;
+    if (!aligned16(src_k_caches[l]) || !aligned16(src_v_caches[l]) || !aligned16(dst_k_caches[l]) ||
+        !aligned16(dst_v_caches[l]))
+      return PKV_ERR_ALIGN;
+  }
+  const long long chunk_wgs = (block_bytes / 16 + 255) / 256;
+  if ((long long)num_pairs * chunk_wgs > (1LL << 31) - 1) return PKV_ERR_SHAPE;
+  // Host pools and a host pair list are reached through their mapped addresses.
+  std::vector<void*> sk(num_layers), sv(num_layers), dk(num_layers), dv(num_layers);
+  for (int l = 0; l < num_layers; ++l) {
+    int st = gpu_address(src_k_caches[l], &sk[l]);
+    if (st == PKV_OK) st = gpu_address(src_v_caches[l], &sv[l]);
+    if (st == PKV_OK) st = gpu_address(dst_k_caches[l], &dk[l]);
+    if (st == PKV_OK) st = gpu_address(dst_v_caches[l], &dv[l]);
+    if (st != PKV_OK) return st;
+  }
+  void* pairs = nullptr;
+  const int st = gpu_address(src_dst_pairs, &pairs);
+  if (st != PKV_OK) return st;
+  return hip_status(pkv::launch_move_blocks(const_cast<const void* const*>(sk.data()), const_cast<const void* const*>(sv.data()), dk.data(), dv.data(), num_layers,
+                                            static_cast<const int64_t*>(pairs), num_pairs, block_bytes,
+                                            num_src_blocks, num_dst_blocks, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -49,45 +49,56 @@ hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, int in_type, int kv
 
 constexpr int kMaxCopyLayers = 64;
 
-struct CopyArgs {
-  void* k[kMaxCopyLayers];
-  void* v[kMaxCopyLayers];
-  const int64_t* pairs;       // [num_pairs, 2] (src, dst)
-  int64_t block_bytes;        // bytes of one block of one layer's K (or V) cache
-  int64_t num_blocks;
+// Whole-block moves between two pools (the same pool for copy-on-write; a GPU pool and a
+// pinned host pool for swapping). Every pointer is one layer's K or V pool, addressable by
+// the GPU: device memory, or host memory pinned and mapped by the HIP runtime.
+struct MoveArgs {
+  const void* src_k[kMaxCopyLayers];
+  const void* src_v[kMaxCopyLayers];
+  void* dst_k[kMaxCopyLayers];
+  void* dst_v[kMaxCopyLayers];
+  const int64_t* pairs;       // [num_pairs, 2] (src block, dst block)
+  int64_t block_bytes;        // bytes of one block of one layer's K (or V) pool
+  int64_t num_src_blocks, num_dst_blocks;
   int num_pairs;
   int chunk_wgs;              // workgroups per (pair, layer, tensor)
 };
 
 // blockIdx.x = pair * chunk_wgs + chunk group, blockIdx.y = layer, blockIdx.z = 0 (K) / 1 (V).
-__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
+// Each thread moves one 16-byte chunk; a pair with an id out of range is skipped.
+__global__ __launch_bounds__(256) void move_blocks_kernel(const MoveArgs a) {
   const int pair = blockIdx.x / a.chunk_wgs;
   const int64_t chunk = (int64_t)(blockIdx.x % a.chunk_wgs) * 256 + threadIdx.x;
   if (chunk * 16 >= a.block_bytes) return;
   const int64_t src = a.pairs[2 * pair], dst = a.pairs[2 * pair + 1];
-  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
-  uint8_t* base = (uint8_t*)(blockIdx.z == 0 ? a.k[blockIdx.y] : a.v[blockIdx.y]);
-  const u32x4 x = *(const u32x4*)(base + src * a.block_bytes + chunk * 16);
-  *(u32x4*)(base + dst * a.block_bytes + chunk * 16) = x;
+  if (src < 0 || src >= a.num_src_blocks || dst < 0 || dst >= a.num_dst_blocks) return;
+  const uint8_t* from = (const uint8_t*)(blockIdx.z == 0 ? a.src_k[blockIdx.y] : a.src_v[blockIdx.y]);
+  uint8_t* to = (uint8_t*)(blockIdx.z == 0 ? a.dst_k[blockIdx.y] : a.dst_v[blockIdx.y]);
+  const u32x4 x = *(const u32x4*)(from + src * a.block_bytes + chunk * 16);
+  *(u32x4*)(to + dst * a.block_bytes + chunk * 16) = x;
 }
 
-hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers,
-                              const int64_t* pairs, int num_pairs, int64_t block_bytes, int64_t num_blocks,
+hipError_t launch_move_blocks(const void* const* src_k, const void* const* src_v, void* const* dst_k,
+                              void* const* dst_v, int num_layers, const int64_t* pairs, int num_pairs,
+                              int64_t block_bytes, int64_t num_src_blocks, int64_t num_dst_blocks,
                               hipStream_t stream) {
   if (num_pairs == 0 || num_layers == 0) return hipSuccess;
-  CopyArgs a;
+  MoveArgs a;
   a.pairs = pairs;
   a.block_bytes = block_bytes;
-  a.num_blocks = num_blocks;
+  a.num_src_blocks = num_src_blocks;
+  a.num_dst_blocks = num_dst_blocks;
   a.num_pairs = num_pairs;
   a.chunk_wgs = (int)((block_bytes / 16 + 255) / 256);
   for (int l0 = 0; l0 < num_layers; l0 += kMaxCopyLayers) {
     const int nl = num_layers - l0 < kMaxCopyLayers ? num_layers - l0 : kMaxCopyLayers;
     for (int l = 0; l < nl; ++l) {
-      a.k[l] = k_caches[l0 + l];
-      a.v[l] = v_caches[l0 + l];
+      a.src_k[l] = src_k[l0 + l];
+      a.src_v[l] = src_v[l0 + l];
+      a.dst_k[l] = dst_k[l0 + l];
+      a.dst_v[l] = dst_v[l0 + l];
     }
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs * a.chunk_wgs, nl, 2), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(move_blocks_kernel, dim3(num_pairs * a.chunk_wgs, nl, 2), dim3(256), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

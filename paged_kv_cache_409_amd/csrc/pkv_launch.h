@@ -81,7 +81,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int q_type, int kv_type, int 
 hipError_t launch_decode_valu(const DecodeArgs& a, int q_type, int kv_type, int head_dim, hipStream_t s);
 hipError_t launch_decode_reduce(const ReduceArgs& a, int q_type, int head_dim, hipStream_t s);
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, int in_type, int kv_type, hipStream_t s);
-hipError_t launch_copy_blocks(void* const* k, void* const* v, int num_layers, const int64_t* pairs, int num_pairs,
-                              int64_t block_bytes, int64_t num_blocks, hipStream_t s);
+// Copy-on-write (src pools = dst pools) and swapping (a GPU pool and a host pool) move whole
+// blocks with the same kernel.
+hipError_t launch_move_blocks(const void* const* src_k, const void* const* src_v, void* const* dst_k,
+                              void* const* dst_v, int num_layers, const int64_t* pairs, int num_pairs,
+                              int64_t block_bytes, int64_t num_src_blocks, int64_t num_dst_blocks, hipStream_t s);
 
 }  // namespace pkv

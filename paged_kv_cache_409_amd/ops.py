@@ -189,3 +189,32 @@ def copy_blocks(k_caches, v_caches, src_dst_pairs, stream=None) -> None:
     st = _lib.load().pkv_copy_blocks(kp, vp, n, src_dst_pairs.data_ptr(), src_dst_pairs.shape[0], block_bytes,
                                      ref.shape[0], _stream(stream))
     _check("pkv_copy_blocks", st)
+
+
+def swap_blocks(src_k_caches, src_v_caches, dst_k_caches, dst_v_caches, src_dst_pairs, stream=None) -> None:
+    """For each (src, dst) pair and layer: dst pool[dst] = src pool[src], K and V. One side is
+    the GPU pool, the other a pool in pinned host memory (torch pin_memory=True)."""
+    n = len(src_k_caches)
+    if not (len(src_v_caches) == len(dst_k_caches) == len(dst_v_caches) == n):
+        raise ValueError("the four pool lists differ in length")
+    if not src_dst_pairs.is_cuda and not src_dst_pairs.is_pinned():
+        raise ValueError("src_dst_pairs must be a device tensor or pinned host memory")
+    if src_dst_pairs.dtype != torch.int64 or src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be int64 [num_pairs, 2]")
+    src, dst = src_k_caches[0], dst_k_caches[0]
+    for pools, ref in ((src_k_caches, src), (src_v_caches, src), (dst_k_caches, dst), (dst_v_caches, dst)):
+        for c in pools:
+            if not (c.is_cuda or c.is_pinned()):
+                raise ValueError("pools must be device tensors or pinned host tensors")
+            if not c.is_contiguous():
+                raise ValueError("pools must be contiguous")
+            if c.shape[1:] != ref.shape[1:] or c.dtype != ref.dtype or c.shape[0] != ref.shape[0]:
+                raise ValueError("pools on one side must share shape and dtype")
+    if src.shape[1:] != dst.shape[1:] or src.dtype != dst.dtype:
+        raise ValueError("source and destination blocks differ in shape or dtype")
+    ptrs = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])
+    block_bytes = src[0].numel() * src.element_size()
+    st = _lib.load().pkv_swap_blocks(ptrs(src_k_caches), ptrs(src_v_caches), ptrs(dst_k_caches), ptrs(dst_v_caches),
+                                     n, src_dst_pairs.data_ptr(), src_dst_pairs.shape[0], block_bytes,
+                                     src.shape[0], dst.shape[0], _stream(stream))
+    _check("pkv_swap_blocks", st)

@@ -142,3 +142,20 @@ def test_prefill_argument_errors_are_reported_before_any_launch():
     assert pf(q=8) == -6                            # misaligned
     assert pf(qstride=1028) == -6                   # not a multiple of 8 elements
     assert pf(S=0) == 0 and pf(T=0) == 0 and pf(maxq=0) == 0    # nothing to do
+
+
+def test_swap_argument_errors():
+    # Rejected before any pointer is looked at or any launch: fake pointers are safe.
+    lib = _lib.load()
+    ptrs = (ctypes.c_void_p * 1)(16)
+    sw = lib.pkv_swap_blocks
+    assert sw(ptrs, ptrs, ptrs, ptrs, 1, 16, 0, 4096, 64, 32, None) == 0        # no pairs: no-op
+    assert sw(ptrs, ptrs, ptrs, ptrs, 0, 16, 4, 4096, 64, 32, None) == 0        # no layers: no-op
+    assert sw(ptrs, ptrs, ptrs, ptrs, 1, 16, 2, 4095, 64, 32, None) == -2       # not a multiple of 16
+    assert sw(ptrs, ptrs, ptrs, ptrs, 1, 16, 2, 4096, 64, 0, None) == -2        # empty destination pool
+    assert sw(None, ptrs, ptrs, ptrs, 1, 16, 2, 4096, 64, 32, None) == -1
+    assert sw(ptrs, ptrs, ptrs, ptrs, 1, None, 2, 4096, 64, 32, None) == -1
+    nullp = (ctypes.c_void_p * 1)(None)
+    assert sw(ptrs, ptrs, nullp, ptrs, 1, 16, 2, 4096, 64, 32, None) == -1
+    odd = (ctypes.c_void_p * 1)(8)
+    assert sw(ptrs, ptrs, odd, ptrs, 1, 16, 2, 4096, 64, 32, None) == -6

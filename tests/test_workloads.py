@@ -153,3 +153,17 @@ def test_fp8_pool_codes_are_never_nan(monkeypatch):
     monkeypatch.setattr(torch.Tensor, "geometric_", lambda self, p, generator=None: self.fill_(0.0))
     zero = gen._fp8_codes((4096,), "cpu", 2).numpy()
     assert ((zero >> 3) & 0xF).max() == 14
+
+
+@pytest.mark.parametrize("name", ["swap_tiny", "swap_70b"])
+def test_swap_pairs_are_distinct_and_in_range(name):
+    from workloads import SWAP_CONFIGS, make_swap_pairs
+    cfg = SWAP_CONFIGS[name]
+    out_pairs, in_pairs = make_swap_pairs(cfg)
+    n = cfg.swap_blocks
+    assert out_pairs.shape == (n, 2) and in_pairs.shape == (n, 2)
+    assert len(set(out_pairs[:, 0])) == n and len(set(out_pairs[:, 1])) == n and len(set(in_pairs[:, 1])) == n
+    assert (out_pairs[:, 1] == in_pairs[:, 0]).all()                 # what went out comes back
+    assert not set(out_pairs[:, 0]) & set(in_pairs[:, 1])            # into blocks that were free
+    assert out_pairs[:, 0].max() < cfg.gpu_blocks and in_pairs[:, 1].max() < cfg.gpu_blocks
+    assert out_pairs[:, 1].max() < cfg.host_blocks

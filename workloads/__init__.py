@@ -5,3 +5,4 @@ quantisation or cache-write arithmetic lives here.
 """
 from .configs import ALL_CONFIGS, CONFIGS, PREFILL_CONFIGS, WorkloadConfig  # noqa: F401
 from .gen import Batch, Layout, make_batch, make_layout  # noqa: F401
+from .swap import SWAP_CONFIGS, SwapConfig, make_swap_pairs, make_swap_pools  # noqa: F401
