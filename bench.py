@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config llama2_70b_gqa]
     python bench.py --config prefill_70b_gqa      (a prefill-chunk step, see prefill_bench)
+    python bench.py --config swap_70b             (blocks out to pinned host memory and back, see swap_bench)
 
 A step is the whole hot path over one synthetic batch: copy-on-write block copies
 (when the batch has any), the cache write of every sequence's new token, then
@@ -33,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
 PEAK_MFMA_TFLOPS = 2500.0      # MI355X published dense bf16 / fp16 matrix-core rate
+PEAK_HOST_LINK_GBS = 64.0      # PCIe 5.0 x16, one direction: the MI355X host link
 CPU_SAMPLE_SECONDS = 12.0      # target length of the timed oracle sample
 DECODE_SOURCES = ("paged_kv_cache_409_amd/csrc/decode_mfma.hip", "paged_kv_cache_409_amd/csrc/decode_valu.hip",
                   "paged_kv_cache_409_amd/csrc/decode_common.h", "paged_kv_cache_409_amd/csrc/pkv_device.h")
@@ -94,6 +96,9 @@ def main() -> int:
         return copy_calibration(args, dev)
     if args.config in PREFILL_CONFIGS:
         return prefill_bench(args, PREFILL_CONFIGS[args.config], dev)
+    from workloads import SWAP_CONFIGS
+    if args.config in SWAP_CONFIGS:
+        return swap_bench(args, SWAP_CONFIGS[args.config], dev)
     cfg = CONFIGS[args.config]
     batches = [make_batch(cfg, dev, replica=r) for r in range(args.replicas)]
     lay = batches[0].layout
@@ -319,6 +324,121 @@ def prefill_cpu_baseline(cfg, b):
             "tokens_per_s": round(float(n[seqs].sum()) / dt, 2), "cores": 1, "kind": "oracle",
             "sample": f"{len(seqs)} sequence runs over the {cfg.num_seqs} sequences (all rows and heads, "
                       f"shortest first), float64 numpy oracle on one host thread, {dt:.1f} s"}
+
+
+def swap_bench(args, cfg, dev) -> int:
+    """One swap step: a preempted request's blocks (scattered, every layer, K and V) go out
+    to pinned host memory, then come back into other free GPU blocks. `value` is bytes moved
+    over the host link per second, both directions together; `roofline` compares it with
+    the link's one-direction peak (the two directions run one after the other). Beside it,
+    one contiguous runtime copy of the same size each way gives the link rate the DMA
+    engines reach."""
+    import torch
+
+    import paged_kv_cache_409_amd as pkv
+    from workloads import make_swap_pairs, make_swap_pools
+
+    gpu = make_swap_pools(cfg, "gpu", dev)
+    host = make_swap_pools(cfg, "host", dev, pin=True)
+    gk, gv = [k for k, _ in gpu], [v for _, v in gpu]
+    hk, hv = [k for k, _ in host], [v for _, v in host]
+    out_np, in_np = make_swap_pairs(cfg)
+    out_pairs, in_pairs = torch.from_numpy(out_np).to(dev), torch.from_numpy(in_np).to(dev)
+    nbytes = cfg.bytes_per_direction
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pkv.swap_blocks(gk, gv, hk, hv, out_pairs)
+        if ev is not None:
+            ev[1].record()
+        pkv.swap_blocks(hk, hv, gk, gv, in_pairs)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    out_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
+    in_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
+    # Contiguous runtime copies of the same size, for the DMA engines' link rate.
+    dsrc = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    hbuf = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+    hbuf.copy_(dsrc, non_blocking=True)
+    torch.cuda.synchronize()
+    c0, c1, c2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    c0.record()
+    hbuf.copy_(dsrc, non_blocking=True)
+    c1.record()
+    dsrc.copy_(hbuf, non_blocking=True)
+    c2.record()
+    torch.cuda.synchronize()
+    dma_out, dma_in = c0.elapsed_time(c1), c1.elapsed_time(c2)
+    gbs = lambda ms: round(nbytes / (ms * 1e-3) / 1e9, 2)
+    achieved = 2 * nbytes / ((out_ms.mean() + in_ms.mean()) * 1e-3) / 1e9
+    result = {
+        "metric": "block swap GPU <-> pinned host: achieved GB/s over the host link (% of its one-direction peak)",
+        "value": round(2 * nbytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"kv {cfg.kv_dtype} (bytes moved as they are)",
+        "data": "synthetic",
+        "config": {"workload": cfg.description, "num_layers": cfg.num_layers, "num_kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "block_bytes": cfg.block_bytes, "blocks_per_layer": cfg.swap_blocks,
+                   "bytes_per_direction": nbytes, "parallelism": "single GPU",
+                   "step": "swap_blocks GPU->host (out) + swap_blocks host->GPU (in)"},
+        "swap_out_GBps": gbs(float(out_ms.mean())), "swap_in_GBps": gbs(float(in_ms.mean())),
+        "swap_us": {"out_mean": round(float(out_ms.mean()) * 1e3, 1), "in_mean": round(float(in_ms.mean()) * 1e3, 1)},
+        "dma_contiguous_GBps": {"out": gbs(dma_out), "in": gbs(dma_in)},
+        "roofline": {"bound": "host-link", "achieved": round(achieved, 2), "peak": PEAK_HOST_LINK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HOST_LINK_GBS, 4), "traffic": None,
+                     "kernel": "move_blocks_kernel"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = swap_cpu_baseline(cfg, gk, gv, hk, hv, out_np)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def swap_cpu_baseline(cfg, gk, gv, hk, hv, out_pairs):
+    """Time the swap oracle (numpy block copies into copies of the destination pools) on host
+    copies of the pools, single-threaded, for about CPU_SAMPLE_SECONDS."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import cache_ops
+    to_np = lambda ts: [t.detach().cpu().numpy() if t.element_size() == 1 else
+                        t.detach().cpu().view(torch.int16).numpy() for t in ts]
+    sk, sv, dk, dv = to_np(gk), to_np(gv), to_np(hk), to_np(hv)
+    runs, dt = 0, 0.0
+    with threadpool_limits(limits=1):
+        while dt < CPU_SAMPLE_SECONDS:
+            t0 = time.perf_counter()
+            cache_ops.swap_blocks(sk, sv, dk, dv, out_pairs)
+            dt += time.perf_counter() - t0
+            runs += 1
+    return {"value": round(runs * cfg.bytes_per_direction / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{runs} swap-outs of the whole case ({cfg.bytes_per_direction} bytes each) between host "
+                      f"arrays, numpy oracle on one host thread, {dt:.1f} s"}
 
 
 def copy_calibration(args, dev) -> int:
