@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config llama2_70b_gqa]
     python bench.py --config prefill_70b_gqa      (a prefill-chunk step, see prefill_bench)
     python bench.py --config swap_70b             (blocks out to pinned host memory and back, see swap_bench)
+    python bench.py --config block_manager        (host bookkeeping of decode steps, see block_manager_bench)
 
 A step is the whole hot path over one synthetic batch: copy-on-write block copies
 (when the batch has any), the cache write of every sequence's new token, then
@@ -83,6 +84,9 @@ def main() -> int:
         print("bench.py measures one GPU: decode attention shards by kv head or sequence with no exchange, "
               "and this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
         return 2
+
+    if args.config == "block_manager":
+        return block_manager_bench(args)
 
     import torch
 
@@ -439,6 +443,81 @@ def swap_cpu_baseline(cfg, gk, gv, hk, hv, out_pairs):
             "kind": "oracle",
             "sample": f"{runs} swap-outs of the whole case ({cfg.bytes_per_direction} bytes each) between host "
                       f"arrays, numpy oracle on one host thread, {dt:.1f} s"}
+
+
+def block_manager_bench(args) -> int:
+    """Host bookkeeping of decode steps with the C++ block manager: 64 requests whose
+    500-token prompts share a 256-token system prompt (prefix caching on), 4 beams each;
+    a step appends one token to each of the 256 beams (slots, copy-on-write pairs) and
+    builds their block tables. Timed against the Python block pool the workloads are laid
+    out with, on the same history. No GPU is involved."""
+    from paged_kv_cache_409_amd.block_manager import BlockManager
+    from workloads.blocks import BlockPool, Sequence
+
+    R, B, prompt_len, sys_len, P, NB = 64, 4, 500, 256, 16, 32768
+    steps = max(args.steps, 1) * 4
+    rng = np.random.default_rng(40910)
+    system = rng.integers(0, 32000, size=sys_len).astype(np.int32)
+    prompts = [np.concatenate([system, rng.integers(0, 32000, size=prompt_len - sys_len).astype(np.int32)])
+               for _ in range(R)]
+    max_blocks = (prompt_len + steps + P - 1) // P
+
+    def run_cpp():
+        bm = BlockManager(NB, block_size=P, prefix_caching=True)
+        cached = 0
+        for r in range(R):
+            _, c = bm.add_sequence(1000 * r, prompt_len, prompts[r])
+            cached += c
+            for b in range(B):
+                bm.fork(1000 * r, 1000 * r + 1 + b)
+            bm.free(1000 * r)
+        ids = np.array([1000 * r + 1 + b for r in range(R) for b in range(B)], dtype=np.int64)
+        tok = np.zeros(len(ids), dtype=np.int32)
+        t0 = time.perf_counter()
+        copies = 0
+        for _ in range(steps):
+            _, pairs = bm.append_batch(ids, tok)
+            copies += len(pairs)
+            bm.block_tables(ids, max_blocks)
+        return time.perf_counter() - t0, copies, cached
+
+    def run_python():
+        pool = BlockPool(NB, P)
+        seqs = []
+        for r in range(R):
+            root = Sequence(pool)
+            root.extend(prompt_len)
+            seqs += [root.fork() for _ in range(B)]
+            root.free()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            for sq in seqs:
+                sq.append_slot()
+            tables = np.zeros((len(seqs), max_blocks), dtype=np.int32)
+            for i, sq in enumerate(seqs):
+                tables[i, :len(sq.blocks)] = sq.blocks
+        return time.perf_counter() - t0
+
+    dt, copies, cached = run_cpp()
+    dt_py = run_python()
+    n = R * B * steps
+    result = {
+        "metric": "block-manager bookkeeping of decode steps: sequence-steps/s (host, C++)",
+        "value": round(n / dt, 1), "unit": "sequence-steps/s", "n_gpus": 0, "steps": steps, "warmup": 0,
+        "ms_per_step": round(dt / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32 / int64 (block ids, slots)", "data": "synthetic",
+        "config": {"workload": f"{R} requests x {B} beams, {prompt_len}-token prompts sharing a {sys_len}-token "
+                               f"system prompt, prefix caching on, {NB}-block pool, block size {P}",
+                   "copy_on_write_pairs": copies, "prompt_tokens_served_from_cache": cached,
+                   "step": "append one token to every beam (slots, copy pairs) + block tables of all beams"},
+        "us_per_step": round(dt / steps * 1e6, 1),
+        "roofline": None,
+        "cpu_baseline": {"value": round(n / dt_py, 1), "unit": "sequence-steps/s", "cores": 1,
+                         "kind": "python reference pool (workloads/blocks.py)",
+                         "sample": f"the same {steps} steps without prefix caching, {dt_py:.2f} s"},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def copy_calibration(args, dev) -> int:

@@ -1,4 +1,4 @@
-"""ctypes loader for libpkv.so: symbol signatures of include/pkv.h, nothing else.
+"""ctypes loader for libpkv.so: symbol signatures of include/*.h, nothing else.
 
 The library is built in-tree by `python -m paged_kv_cache_409_amd.build`. There is
 no fallback: if the library is missing or cannot be loaded, every call fails
@@ -15,7 +15,7 @@ PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 1, 2, 3
 
 _c_int, _c_i64, _c_f, _c_p, _c_sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
-# name -> (restype, argtypes), exactly as declared in include/pkv.h
+# name -> (restype, argtypes), exactly as declared in include/pkv.h and include/pkv_block_manager.h
 SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_c_int]),
     "pkv_api_version": (_c_int, []),
@@ -55,6 +55,21 @@ SIGNATURES = {
     "pkv_copy_blocks": (_c_int, [
         ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_int,   # k_caches v_caches num_layers
         _c_p, _c_int, _c_i64, _c_i64, _c_p]),                 # pairs num_pairs block_bytes num_blocks stream
+    # include/pkv_block_manager.h (host-side bookkeeping)
+    "pkv_bm_create": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_p)]),
+    "pkv_bm_destroy": (None, [_c_p]),
+    "pkv_bm_add_sequence": (_c_int, [_c_p, _c_i64, _c_p, _c_int, _c_p, ctypes.POINTER(_c_int)]),
+    "pkv_bm_append": (_c_int, [_c_p, _c_i64, _c_p, _c_int, _c_p, _c_p, _c_int, ctypes.POINTER(_c_int)]),
+    "pkv_bm_append_batch": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_p, _c_p, _c_int, ctypes.POINTER(_c_int)]),
+    "pkv_bm_fork": (_c_int, [_c_p, _c_i64, _c_i64]),
+    "pkv_bm_free": (_c_int, [_c_p, _c_i64]),
+    "pkv_bm_block_tables": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, ctypes.c_int32, _c_p]),
+    "pkv_bm_swap_out": (_c_int, [_c_p, _c_i64, _c_p, _c_int, ctypes.POINTER(_c_int)]),
+    "pkv_bm_swap_in": (_c_int, [_c_p, _c_i64, _c_p, _c_int, ctypes.POINTER(_c_int)]),
+    "pkv_bm_num_free": (_c_int, [_c_p, ctypes.POINTER(_c_int), ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
+    "pkv_bm_refcount": (_c_int, [_c_p, _c_int, ctypes.POINTER(_c_int)]),
+    "pkv_bm_sequence_info": (_c_int, [_c_p, _c_i64, ctypes.POINTER(_c_int), ctypes.POINTER(_c_int),
+                                      ctypes.POINTER(_c_int)]),
 }
 
 _lib = None

@@ -2,8 +2,9 @@
 
     python -m paged_kv_cache_409_amd.build [--verbose]
 
-Compiles every csrc/*.hip to an object in csrc/_build/ (in parallel) and links
-paged_kv_cache_409_amd/libpkv.so. Always rebuilds.
+Compiles every csrc/*.hip (device code, hipcc) and csrc/*.cpp (host code, g++) to an
+object in csrc/_build/ (in parallel) and links paged_kv_cache_409_amd/libpkv.so. Always
+rebuilds.
 """
 from __future__ import annotations
 
@@ -34,6 +35,16 @@ COMMON = [
 FILE_FLAGS = {"prefill_mfma.hip": ["-fno-honor-nans"]}
 
 
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), "/opt/rocm/llvm/bin/clang++"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler found")
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -57,9 +68,13 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     os.makedirs(BUILD, exist_ok=True)
     sources = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    host_sources = sorted(f for f in os.listdir(CSRC) if f.endswith(".cpp"))
     objs = [os.path.join(BUILD, s[:-4] + ".o") for s in sources]
+    host_objs = [os.path.join(BUILD, s[:-4] + ".host.o") for s in host_sources]
     jobs = [[cc, *COMMON, *FILE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
             for s, o in zip(sources, objs)]
+    jobs += [[cxx(), *HOST_FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(host_sources, host_objs)]
+    objs += host_objs
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"

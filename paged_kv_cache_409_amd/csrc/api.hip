@@ -4,6 +4,7 @@
 #include <vector>
 
 #include "pkv.h"
+#include "pkv_block_manager.h"
 #include "pkv_launch.h"
 
 
@@ -100,6 +101,9 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_ALIGN: return "a device pointer or stride is not 16-byte aligned";
     case PKV_ERR_HIP: return "the HIP runtime reported an error";
+    case PKV_ERR_NO_BLOCKS: return "not enough free blocks";
+    case PKV_ERR_SEQ: return "unknown or duplicate sequence id, or the sequence is swapped the other way";
+    case PKV_ERR_CAPACITY: return "an output array is too small";
     default: return "unknown status";
   }
 }
