@@ -103,7 +103,8 @@ def main() -> int:
     from workloads import SWAP_CONFIGS
     if args.config in SWAP_CONFIGS:
         return swap_bench(args, SWAP_CONFIGS[args.config], dev)
-    cfg = CONFIGS[args.config]
+    from workloads import BLOCK_SIZE_CONFIGS
+    cfg = {**CONFIGS, **BLOCK_SIZE_CONFIGS}[args.config]
     batches = [make_batch(cfg, dev, replica=r) for r in range(args.replicas)]
     lay = batches[0].layout
     kv_logical = kv_bytes_logical(cfg, lay.context_lens)

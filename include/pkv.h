@@ -32,9 +32,11 @@
  * - Calls are reentrant; the library holds no global state.
  *
  * Cache layout (chosen for gfx950): k_cache and v_cache are separate tensors of
- * shape [num_blocks, num_kv_heads, block_size, head_dim] with block_size = 16, so one
- * kv head's slice of one block (16 token rows) is a single contiguous tile that a
- * wavefront reads with 16-byte loads. A slot is the flat index block * 16 + offset.
+ * shape [num_blocks, num_kv_heads, block_size, head_dim] with block_size 16 (the
+ * default of the pages), 32 or 64, so one kv head's slice of one block is a contiguous
+ * run of 16-token tiles that a wavefront reads with 16-byte loads. A slot is the flat
+ * index block * block_size + offset. ("vLLM 推理优化技术深度调研报告", 维度四.5 weighs
+ * bigger blocks; on MI355X 16 is both the fastest and the least wasteful.)
  *
  * The method follows the pages on PagedAttention: the KV cache is cut into blocks
  * of 16 token slots, placed anywhere in a shared pool and found through a
@@ -112,7 +114,7 @@ size_t pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int num
  *   out            [num_seqs, num_q_heads, head_dim]          q_dtype (written)
  *   q              [num_seqs, num_q_heads, head_dim]          q_dtype; sequence stride
  *                  q_seq_stride elements (0 = num_q_heads * head_dim)
- *   k_cache/v_cache[num_blocks, num_kv_heads, 16, head_dim]   kv_dtype
+ *   k_cache/v_cache[num_blocks, num_kv_heads, block_size, head_dim]   kv_dtype
  *   block_tables   [num_seqs, max_blocks_per_seq] int32       physical block ids
  *   context_lens   [num_seqs] int32                            tokens to attend, <= max_context_len
  *   q_dtype        PKV_F16 or PKV_BF16
@@ -127,8 +129,8 @@ size_t pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int num
  *                  (may be NULL when that size is 0)
  *
  * Supported: head_dim 64 or 128; num_q_heads a multiple of num_kv_heads with group
- * size 1..16; block_size 16. Group size 1 runs on the vector ALUs, larger groups on
- * the matrix cores.
+ * size 1..16; block_size 16, 32 or 64. Group size 1 runs on the vector ALUs, larger
+ * groups on the matrix cores.
  */
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, const int32_t* context_lens,
@@ -186,7 +188,7 @@ int pkv_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
  *   query_start_loc[num_seqs + 1] int32: sequence s owns rows [qsl[s], qsl[s+1]) of q
  *                  and out; non-decreasing, qsl[num_seqs] <= num_tokens
  *   context_lens   [num_seqs] int32: context length after the chunk (chunk included),
- *                  at least n_s and at most max_blocks_per_seq * 16
+ *                  at least n_s and at most max_blocks_per_seq * block_size
  *   max_query_len  upper bound of every n_s (host-side hint; sets the grid)
  *   scale          logit scale, finite and > 0
  * Every other argument is as for pkv_paged_attention_decode. No workspace is needed.
@@ -194,7 +196,8 @@ int pkv_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
  * Rows outside every sequence's range are not written. A sequence whose offsets fall
  * outside [0, num_tokens] is skipped; a chunk longer than max_query_len or than its
  * context is cut to the shorter, and only its first rows are written.
- * Supported: head_dim 64 or 128; any group size; block_size 16; matrix cores throughout.
+ * Supported: head_dim 64 or 128; any group size; block_size 16, 32 or 64; matrix cores
+ * throughout.
  */
 int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* block_tables, const int32_t* context_lens,
@@ -211,8 +214,8 @@ int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache, c
  *
  *   key/value      [num_tokens, num_kv_heads, head_dim] in_dtype; token strides
  *                  key_stride / value_stride elements (0 = num_kv_heads * head_dim)
- *   slot_mapping   [num_tokens] int64; slot = block * 16 + offset; a negative slot is skipped
- *   k_cache/v_cache[num_blocks, num_kv_heads, 16, head_dim] kv_dtype (one layer)
+ *   slot_mapping   [num_tokens] int64; slot = block * block_size + offset; a negative slot is skipped
+ *   k_cache/v_cache[num_blocks, num_kv_heads, block_size, head_dim] kv_dtype (one layer)
  *   in_dtype       PKV_F16 or PKV_BF16
  *   kv_dtype       in_dtype (the row is copied bit for bit) or PKV_FP8_E4M3, where every
  *                  element is stored as E4M3FN(fl32(x / scale)): IEEE fp32 division,
@@ -240,7 +243,7 @@ int pkv_reshape_and_cache(const void* key, const void* value, const int64_t* slo
  *                  num_blocks blocks of block_bytes bytes
  *   src_dst_pairs  device [num_pairs, 2] int64
  *   block_bytes    bytes of one block of one layer's K (= V) cache:
- *                  num_kv_heads * 16 * head_dim * element size; a multiple of 16
+ *                  num_kv_heads * block_size * head_dim * element size; a multiple of 16
  *
  * Every dst must be distinct and must not be a src in the same call (a copy goes to a
  * freshly taken block); num_pairs = 0 is a no-op.

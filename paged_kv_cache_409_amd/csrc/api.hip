@@ -64,6 +64,11 @@ int make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
+// log2(block_size / 16) for the supported block sizes 16, 32 and 64; -1 otherwise.
+int block_shift_of(int block_size) {
+  return block_size == 16 ? 0 : block_size == 32 ? 1 : block_size == 64 ? 2 : -1;
+}
+
 // The address under which the GPU reaches p: p itself for device memory, the mapped address
 // for host memory pinned through the HIP runtime. Pageable (unregistered) host memory is
 // refused, since a kernel touching it would fault.
@@ -147,10 +152,14 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     return PKV_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
   if ((long long)num_seqs * num_q_heads > (1LL << 30)) return PKV_ERR_SHAPE;
-  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * 16) return PKV_ERR_SHAPE;
   if (!is16bit(q_dtype)) return PKV_ERR_DTYPE;
   if (kv_dtype != q_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-  if (block_size != 16 || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
+  const int shift = block_shift_of(block_size);
+  if (shift < 0 || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+  // tiles are named block * 2^shift + sub-tile in an int
+  if ((num_blocks << shift) > 0x7fffffffLL || ((int64_t)max_blocks_per_seq << shift) > 0x7fffffffLL / 16)
+    return PKV_ERR_SHAPE;
   const int group = num_q_heads / num_kv_heads;
   if (group > kMaxGroup) return PKV_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
@@ -200,6 +209,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.num_kv_heads = num_kv_heads;
   a.group = group;
   a.max_blocks = max_blocks_per_seq;
+  a.block_shift = shift;
   a.num_parts = plan.num_parts;
   a.part_blocks = plan.part_tokens / 16;
   // Sequences per workgroup: the matrix-core kernel puts up to 16 / G neighbouring
@@ -211,7 +221,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     per_group = 16 / group < pkv::kMaxSeqsPerGroup ? 16 / group : pkv::kMaxSeqsPerGroup;
     // (list entries keep the logical block index in 16 bits)
     group_mode = per_group > 1 && (long long)per_group * a.part_blocks <= pkv::kMaxGroupListEntries &&
-                 max_blocks_per_seq <= 65536;
+                 ((long long)max_blocks_per_seq << shift) <= 65536;
     if (pkv::mfma_decode_lds_bytes(head_dim, per_group, a.part_blocks, group_mode) > kMaxDynamicLds)
       group_mode = false;
     if (pkv::mfma_decode_lds_bytes(head_dim, per_group, a.part_blocks, group_mode) > kMaxDynamicLds)
@@ -230,7 +240,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.slot_mapping = tok ? tok->slot_mapping : nullptr;
   a.key_stride = key_stride;
   a.value_stride = value_stride;
-  a.num_slots = num_blocks * 16;
+  a.num_slots = num_blocks * block_size;
   a.k_quant = fp8 ? k_scale : 1.0f;
   a.v_quant = fp8 ? v_scale : 1.0f;
 
@@ -250,7 +260,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     r.num_q_heads = num_q_heads;
     r.num_parts = plan.num_parts;
     r.part_tokens = plan.part_tokens;
-    r.max_tokens = max_blocks_per_seq * 16;
+    r.max_tokens = max_blocks_per_seq * block_size;
     r.v_scale = a.v_scale;
     e = pkv::launch_decode_reduce(r, qt, head_dim, s);
   }
@@ -300,7 +310,10 @@ int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache, c
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
   if (!is16bit(q_dtype)) return PKV_ERR_DTYPE;
   if (kv_dtype != q_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-  if (block_size != 16 || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
+  const int shift = block_shift_of(block_size);
+  if (shift < 0 || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
+  if ((num_blocks << shift) > 0x7fffffffLL || ((int64_t)max_blocks_per_seq << shift) > 0x7fffffffLL / 16)
+    return PKV_ERR_SHAPE;
   if (!(std::isfinite(scale) && scale > 0.f)) return PKV_ERR_SHAPE;
   const bool fp8 = kv_dtype == PKV_FP8_E4M3;
   if (fp8 && !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
@@ -327,6 +340,7 @@ int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache, c
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
+  a.block_shift = shift;
   a.q_token_stride = q_token_stride;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
@@ -353,7 +367,8 @@ int pkv_reshape_and_cache(const void* key, const void* value, const int64_t* slo
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
   if (!is16bit(in_dtype)) return PKV_ERR_DTYPE;
   if (kv_dtype != in_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-  if (block_size != 16 || head_dim <= 0 || head_dim % 8 != 0 || head_dim > 1024) return PKV_ERR_UNSUPPORTED;
+  const int shift = block_shift_of(block_size);
+  if (shift < 0 || head_dim <= 0 || head_dim % 8 != 0 || head_dim > 1024) return PKV_ERR_UNSUPPORTED;
   if (kv_dtype == PKV_FP8_E4M3 &&
       !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
     return PKV_ERR_SHAPE;
@@ -376,7 +391,8 @@ int pkv_reshape_and_cache(const void* key, const void* value, const int64_t* slo
   a.v_cache = v_cache;
   a.key_stride = key_stride;
   a.value_stride = value_stride;
-  a.num_slots = num_blocks * 16;
+  a.num_slots = num_blocks * block_size;
+  a.block_shift = shift;
   a.num_tokens = num_tokens;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;

@@ -2,7 +2,7 @@
 //
 // * A decoded token's K and V rows go into the slot the block manager assigned it
 //   (a fresh block is taken only when the current one is full: "vLLM 是什么…", §二).
-//   The slot is the flat index block * 16 + offset; a negative slot is skipped.
+//   The slot is the flat index block * block_size + offset; a negative slot is skipped.
 //   For an fp8 cache each value is quantised on the way in:
 //   code = E4M3FN(fl32(x / scale)), round to nearest even, saturating at +-448, NaN
 //   kept (the pages only say FP8 halves KV memory, "vLLM推理引擎PagedAttention原理与
@@ -25,8 +25,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
   const int64_t t = tid / ((int64_t)chunks * a.num_kv_heads);
   const int64_t slot = a.slot_mapping[t];
   if (slot < 0 || slot >= a.num_slots) return;
-  const int64_t blk = slot / kBlock, off = slot % kBlock;
-  const int64_t dst = ((blk * a.num_kv_heads + h) * kBlock + off) * a.head_dim + 8 * c;
+  const int P = kBlock << a.block_shift;
+  const int64_t blk = slot / P, off = slot % P;
+  const int64_t dst = ((blk * a.num_kv_heads + h) * P + off) * a.head_dim + 8 * c;
   const u32x4 kin = *(const u32x4*)((const uint16_t*)a.key + t * a.key_stride + (int64_t)h * a.head_dim + 8 * c);
   const u32x4 vin = *(const u32x4*)((const uint16_t*)a.value + t * a.value_stride + (int64_t)h * a.head_dim + 8 * c);
   store_cache_chunk<IT, KVT>(kin, a.k_cache, dst, a.k_scale);

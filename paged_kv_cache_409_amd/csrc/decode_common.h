@@ -20,6 +20,7 @@ struct DecodeArgs {
   int64_t num_blocks;
   int num_seqs, num_q_heads, num_kv_heads, group;
   int max_blocks;                 // block-table row length
+  int block_shift;                // a cache block holds kBlock << block_shift tokens
   int num_parts;                  // partitions per sequence (grid dimension)
   int part_blocks;                // KV blocks per partition
   int num_items;                  // workgroups with work: num_seq_groups * num_kv_heads * num_parts
@@ -34,9 +35,23 @@ struct DecodeArgs {
   const void* new_value;          // [S, Hkv, D] q dtype, token stride value_stride elements
   const int64_t* slot_mapping;    // [S]: slot of each new token; negative = no write
   int64_t key_stride, value_stride;
-  int64_t num_slots;              // num_blocks * 16
+  int64_t num_slots;              // num_blocks * block size
   float k_quant, v_quant;         // fp8 scales the new values are divided by
 };
+
+// Cache blocks hold kBlock << shift tokens (16, 32 or 64); the kernels walk a context in
+// tiles of kBlock tokens, tile t lying in block t >> shift. A tile is named by
+// block * 2^shift + (t mod 2^shift), or -1 when its block id is out of the pool.
+__device__ __forceinline__ int tile_name(const int32_t* row, int t, int shift, int64_t num_blocks) {
+  const int b = row[t >> shift];
+  return (b >= 0 && b < num_blocks) ? b * (1 << shift) + (t & ((1 << shift) - 1)) : -1;
+}
+
+// Byte offset of a named tile in one kv head's view of a pool whose blocks are
+// block_stride bytes apart.
+__device__ __forceinline__ int64_t tile_offset(int v, int shift, int64_t block_stride, int tile_bytes) {
+  return (int64_t)(v >> shift) * block_stride + (int64_t)(v & ((1 << shift) - 1)) * tile_bytes;
+}
 
 // Workgroup -> work item. Workgroups are dealt to the 8 XCDs round-robin; this map
 // gives each run of 4 consecutive items (neighbouring sequences, or sequence groups)
@@ -116,7 +131,8 @@ __device__ __forceinline__ TokenChunk load_new_token(const DecodeArgs& a, int s,
                         (int64_t)s * (t.is_v ? a.value_stride : a.key_stride) + (int64_t)g * D + 8 * c;
   t.data = convert_cache_chunk<QT, KVT>(*(const u32x4*)src, t.is_v ? a.v_quant : a.k_quant);
   t.store = t.written;
-  t.dst = t.store ? ((slot / kBlock * a.num_kv_heads + g) * kBlock + slot % kBlock) * D + 8 * c : 0;
+  const int P = kBlock << a.block_shift;
+  t.dst = t.store ? ((slot / P * a.num_kv_heads + g) * P + slot % P) * D + 8 * c : 0;
   return t;
 }
 

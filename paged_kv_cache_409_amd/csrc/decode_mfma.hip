@@ -139,7 +139,8 @@ __device__ __forceinline__ void mfma_tiles(const DecodeArgs& a, const int g, con
       koff[u] = (n * D + qk_d0<KVT>(u, j4)) * 2;                // row n, 8 values
   }
 
-  const int64_t head_stride = (int64_t)Tr::kTileBytes;
+  const int shift = a.block_shift;
+  const int64_t head_stride = (int64_t)Tr::kTileBytes << shift;   // one kv head's slice of a block
   const uint8_t* kbase = (const uint8_t*)a.k_cache + (int64_t)g * head_stride;
   const uint8_t* vbase = (const uint8_t*)a.v_cache + (int64_t)g * head_stride;
   const int64_t block_stride = (int64_t)a.num_kv_heads * head_stride;
@@ -164,11 +165,11 @@ __device__ __forceinline__ void mfma_tiles(const DecodeArgs& a, const int g, con
     t.pos = readfirstlane(pos);
     t.rows = readfirstlane(rows);
     t.readers = (uint32_t)readfirstlane(readers);
-    const bool live = id >= 0 && id < a.num_blocks;
-    const int phys = live ? id : 0;
+    const bool live = id >= 0;                                     // ids are tile names
+    const int64_t off = live ? tile_offset(id, shift, block_stride, Tr::kTileBytes) : 0;
     const uint32_t bytes = live ? (uint32_t)Tr::kTileBytes : 0u;   // 0: loads return zeros
-    const auto rk = make_rsrc(kbase + phys * block_stride, bytes);
-    const auto rv = make_rsrc(vbase + phys * block_stride, bytes);
+    const auto rk = make_rsrc(kbase + off, bytes);
+    const auto rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
     for (int u = 0; u < Tr::kLoads; ++u) t.k[u] = buf_load16<POLICY>(rk, koff[u]);
 #pragma unroll
@@ -351,8 +352,8 @@ __device__ __forceinline__ void mfma_single(const DecodeArgs& a, const int s, co
   const int end = min(ctx, start + a.part_blocks * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
   {
-    const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + (start / kBlock);
-    for (int i = lane; i < nblk; i += kWave) bt_lds[i] = bt[i];
+    const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
+    for (int i = lane; i < nblk; i += kWave) bt_lds[i] = tile_name(row, start / kBlock + i, a.block_shift, a.num_blocks);
   }
   if (writes) stage_new_token<KVT, D>(token, tok_rows);
   u32x4 qb[D / 32];
@@ -398,15 +399,16 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
   // 1. Each wave stages its sequence's block-table slice and context end, and writes its
   //    sequence's new token (fused step).
   const int s = s0 + w;
-  const int ctx = min(a.context_lens[s], a.max_blocks * kBlock);
+  const int ctx = min(a.context_lens[s], (a.max_blocks * kBlock) << a.block_shift);
   const bool writes = owns_new_token(a, ctx, p);
   TokenChunk token = {};
   if (writes) token = load_new_token<QT, KVT, D>(a, s, g);
   const int end = min(ctx, start + PB * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
   {
-    const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + (start / kBlock);
-    for (int i = lane; i < nblk; i += kWave) bts[w * PB + i] = bt[i];
+    const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
+    for (int i = lane; i < nblk; i += kWave)
+      bts[w * PB + i] = tile_name(row, start / kBlock + i, a.block_shift, a.num_blocks);
   }
   if (lane == 0) {
     ends[w] = end;
@@ -539,8 +541,8 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
   // memory latency rather than a chain): this wave's context length and the block ids at
   // logical block i0 of its sequence and of the sequences on either side, and for the
   // group check the same of every sequence of the group (indices clamped into the batch).
-  const int i0 = start / kBlock;
-  const int max_tokens = a.max_blocks * kBlock;
+  const int i0 = (start / kBlock) >> a.block_shift;   // block of the partition's first tile
+  const int max_tokens = (a.max_blocks * kBlock) << a.block_shift;
   const int64_t mb = a.max_blocks;
   const int s = it.s + w;
   const int s_own = min(s, a.num_seqs - 1);

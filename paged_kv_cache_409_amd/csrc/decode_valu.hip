@@ -112,8 +112,8 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, co
   const int end = min(ctx, start + a.part_blocks * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
   {
-    const int32_t* bt = a.block_tables + (int64_t)it.s * a.max_blocks + (start / kBlock);
-    for (int i = lane; i < nblk; i += kWave) bt_lds[i] = bt[i];
+    const int32_t* row = a.block_tables + (int64_t)it.s * a.max_blocks;
+    for (int i = lane; i < nblk; i += kWave) bt_lds[i] = tile_name(row, start / kBlock + i, a.block_shift, a.num_blocks);
   }
   if (writes) stage_new_token<KVT, D>(token, tok_rows);
 
@@ -133,7 +133,8 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, co
   const int patch_tile = writes && token.written ? (ctx - 1) / kBlock - start / kBlock : -1;
   const int patch_row = (ctx - 1) % kBlock;
 
-  const int64_t head_stride = (int64_t)Tr::kTileBytes;
+  const int shift = a.block_shift;
+  const int64_t head_stride = (int64_t)Tr::kTileBytes << shift;   // one kv head's slice of a block
   const uint8_t* kbase = (const uint8_t*)a.k_cache + (int64_t)it.g * head_stride;
   const uint8_t* vbase = (const uint8_t*)a.v_cache + (int64_t)it.g * head_stride;
   const int64_t block_stride = (int64_t)a.num_kv_heads * head_stride;
@@ -141,11 +142,11 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, co
 
   auto load = [&](VTile<QT, KVT, D>& t, int i) {
     const int id = readfirstlane(i < nblk ? bt_lds[i < nblk ? i : 0] : -1);
-    const bool live = id >= 0 && id < a.num_blocks;
-    const int phys = live ? id : 0;
+    const bool live = id >= 0;                                     // ids are tile names
+    const int64_t off = live ? tile_offset(id, shift, block_stride, Tr::kTileBytes) : 0;
     const uint32_t bytes = live ? (uint32_t)Tr::kTileBytes : 0u;   // 0: loads return zeros
-    const auto rk = make_rsrc(kbase + phys * block_stride, bytes);
-    const auto rv = make_rsrc(vbase + phys * block_stride, bytes);
+    const auto rk = make_rsrc(kbase + off, bytes);
+    const auto rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
     for (int u = 0; u < Tr::kLoads; ++u) t.k[u] = buf_load16<POLICY>(rk, off0 + u * 1024);
 #pragma unroll
@@ -260,9 +261,9 @@ __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
   const int start = it.p * a.part_blocks * kBlock;
   // The context length and the block ids at the partition's first logical block of this
   // sequence and its two neighbours, loaded at once (clamped into the batch).
-  const int i0 = start / kBlock;
+  const int i0 = (start / kBlock) >> a.block_shift;   // block of the partition's first tile
   const int s_prev = max(it.s - 1, 0), s_next = min(it.s + 1, a.num_seqs - 1);
-  const int ctx = min(a.context_lens[it.s], a.max_blocks * kBlock);
+  const int ctx = min(a.context_lens[it.s], (a.max_blocks * kBlock) << a.block_shift);
   const int first_prev = a.block_tables[(int64_t)s_prev * a.max_blocks + i0];
   const int first = a.block_tables[(int64_t)it.s * a.max_blocks + i0];
   const int first_next = a.block_tables[(int64_t)s_next * a.max_blocks + i0];

@@ -21,8 +21,9 @@ struct CacheWriteArgs {
   void* k_cache;              // [NB, Hkv, 16, D]
   void* v_cache;
   int64_t key_stride, value_stride;
-  int64_t num_slots;          // NB * 16
+  int64_t num_slots;          // NB * block size
   int num_tokens, num_kv_heads, head_dim;
+  int block_shift;            // block size = 16 << block_shift
   float k_scale, v_scale;
 };
 
@@ -57,6 +58,7 @@ struct PrefillArgs {
   const void* v_cache;            // [NB, Hkv, 16, D]
   const int32_t* block_tables;    // [S, max_blocks]
   const int32_t* context_lens;    // [S], after the chunk
+  int block_shift;                // a cache block holds 16 << block_shift tokens
   const int32_t* query_start_loc; // [S + 1]
   int64_t q_token_stride;
   int64_t num_blocks;

@@ -79,7 +79,7 @@ template <int KVT, int D>
 struct PrefillTraits {
   static constexpr int kThreads = kWave * kPrefillWaves;
   static constexpr int kElem = (KVT == kFP8) ? 1 : 2;              // bytes per cache element
-  static constexpr int kBlockBytes = kBlock * D * kElem;           // one kv head's slice of a block
+  static constexpr int kBlockBytes = kBlock * D * kElem;           // one kv head's slice of a 16-token tile
   static constexpr int kChunksPerBlock = kBlockBytes / 16;
   static constexpr int kLoads = kPrefillKeys * D * kElem / 16 / kThreads;  // per thread, K (or V)
   // LDS rows are padded rather than swizzled, so that every operand read is a per-lane
@@ -109,7 +109,8 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
   const int g = pair / a.num_seqs, s = pair % a.num_seqs;
   const int G = a.group;
 
-  const int ctx = min(max(a.context_lens[s], 0), a.max_blocks * kBlock);
+  const int shift = a.block_shift;   // a cache block holds kBlock << shift tokens, walked in kBlock-token tiles
+  const int ctx = min(max(a.context_lens[s], 0), (a.max_blocks * kBlock) << shift);
   const int q0 = a.query_start_loc[s], q1 = a.query_start_loc[s + 1];
   if (q0 < 0 || q1 < q0 || q1 > a.num_tokens) return;
   const int n = min(min(q1 - q0, a.max_query_len), ctx);
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
   if (row0 >= R) return;
   const int prefix = ctx - n;
   const int kv_end = prefix + (min(R, row0 + kPrefillRows) - 1) / G + 1;   // keys the workgroup needs
-  const int nblk = (kv_end + kBlock - 1) / kBlock;
+  const int ntiles = (kv_end + kBlock - 1) / kBlock;   // 16-token tiles the workgroup reads
   const int n_iter = (kv_end + kPrefillKeys - 1) / kPrefillKeys;
 
   const int t = threadIdx.x, w = readfirstlane(t / kWave), lane = t & (kWave - 1);
@@ -145,18 +146,19 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
   const int wave_hi = wave_live ? prefix + (min(R, wrow0 + kPrefillCols) - 1) / G + 1 : 0;   // last row's
 
   // ---- K/V tiles: global -> registers -> LDS ----------------------------------------------
-  const int64_t head_stride = Tr::kBlockBytes;
+  const int64_t head_stride = (int64_t)Tr::kBlockBytes << shift;   // one kv head's slice of a block
   const int64_t block_stride = (int64_t)a.num_kv_heads * head_stride;
   const uint8_t* kbase = (const uint8_t*)a.k_cache + (int64_t)g * head_stride;
   const uint8_t* vbase = (const uint8_t*)a.v_cache + (int64_t)g * head_stride;
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
-  const int num_blocks = (int)min(a.num_blocks, (int64_t)0x7fffffff);
 
-  // Block ids are staged in an LDS ring of kIdsRing table entries (-1 past the last
-  // block), refilled by the whole workgroup when the tiles reach its end. A tile's four
-  // ids are read from the ring one iteration before its loads are issued.
-  auto fill_ids = [&](int first) {   // entries [first, first + kIdsRing); first is a multiple of kIdsRing
-    for (int k = t; k < kIdsRing; k += Tr::kThreads) ids_lds[k] = first + k < nblk ? bt[first + k] : -1;
+  // The names of the 16-token tiles (block * 2^shift + sub-tile, -1 past the last tile or
+  // for a block id out of the pool) are staged in an LDS ring of kIdsRing entries,
+  // refilled by the whole workgroup when the walk reaches its end. A key tile's four names
+  // are read from the ring one iteration before its loads are issued.
+  auto fill_ids = [&](int first) {   // tiles [first, first + kIdsRing); first is a multiple of kIdsRing
+    for (int k = t; k < kIdsRing; k += Tr::kThreads)
+      ids_lds[k] = first + k < ntiles ? tile_name(bt, first + k, shift, a.num_blocks) : -1;
   };
   auto read_ids = [&](int i) -> u32x4 {   // ids of tile i's four blocks (same address in every lane)
     return *(const u32x4*)(ids_lds + ((i * (kPrefillKeys / kBlock)) & (kIdsRing - 1)));
@@ -176,8 +178,8 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
     for (int u = 0; u < Tr::kLoads; ++u) {
       const int j = (u * Tr::kThreads + w * kWave) / Tr::kChunksPerBlock;
       const int id = j == 0 ? id0 : j == 1 ? id1 : j == 2 ? id2 : id3;
-      const bool live = id >= 0 && id < num_blocks;
-      const int64_t off = (live ? (int64_t)id : 0) * block_stride;
+      const bool live = id >= 0;                                    // ids are tile names
+      const int64_t off = live ? tile_offset(id, shift, block_stride, Tr::kBlockBytes) : 0;
       const uint32_t bytes = live ? (uint32_t)Tr::kBlockBytes : 0u;   // 0: loads return zeros
       const uint32_t c16 = (uint32_t)((u * Tr::kThreads + t) % Tr::kChunksPerBlock) * 16;
       rk[u] = buf_load16<kPolicyCached>(make_rsrc(kbase + off, bytes), c16);

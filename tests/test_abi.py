@@ -76,7 +76,8 @@ def test_decode_argument_errors_are_reported_before_any_launch():
     assert _decode(lib, qt=_lib.PKV_FP8_E4M3) == -3  # q cannot be fp8
     assert _decode(lib, kt=_lib.PKV_F16) == -3       # cache dtype must match q or be fp8
     assert _decode(lib, D=96) == -4
-    assert _decode(lib, P=32) == -4
+    assert _decode(lib, P=48) == -4                  # block sizes 16, 32, 64 only
+    assert _decode(lib, P=8) == -4
     assert _decode(lib, Hq=64, Hkv=2) == -4          # group of 32 heads
     assert _decode(lib, kt=_lib.PKV_FP8_E4M3, ks=0.0) == -2
     assert _decode(lib, out=8) == -6                 # misaligned
@@ -140,7 +141,7 @@ def test_prefill_argument_errors_are_reported_before_any_launch():
     assert pf(qt=_lib.PKV_FP8_E4M3) == -3
     assert pf(kt=_lib.PKV_F16) == -3
     assert pf(D=96) == -4
-    assert pf(P=64) == -4
+    assert pf(P=128) == -4
     assert pf(kt=_lib.PKV_FP8_E4M3, vs=0.0) == -2
     assert pf(q=8) == -6                            # misaligned
     assert pf(qstride=1028) == -6                   # not a multiple of 8 elements

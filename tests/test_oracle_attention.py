@@ -217,3 +217,21 @@ def test_physical_slot_follows_the_block_table():
     assert attention.physical_slot(row, 15, 16) == (7, 15)
     assert attention.physical_slot(row, 16, 16) == (3, 0)
     assert attention.physical_slot(row, 36, 16) == (11, 4)
+
+
+@pytest.mark.parametrize("block_size", [32, 64])
+def test_block_size_changes_only_where_tokens_live(block_size):
+    # The same logical K/V in pools of 16-, 32- and 64-token blocks ("vLLM 推理优化技术深度
+    # 调研报告", 维度四.5 weighs these sizes) gives the same attention, bit for bit.
+    rng = np.random.default_rng(block_size)
+    ctxs = [1, 31, 33, 64, 65, 130]
+    q = f16_bits(rng.standard_normal((len(ctxs), 4, 32)))
+    kb = [f16_bits(rng.standard_normal((c, 2, 32))) for c in ctxs]
+    vb = [f16_bits(rng.standard_normal((c, 2, 32))) for c in ctxs]
+    outs = []
+    for P in (16, block_size):
+        kp, tab = scatter_to_pool(kb, 64 * 16 // P + 8, P, np.random.default_rng(1))
+        vp, _ = scatter_to_pool(vb, 64 * 16 // P + 8, P, np.random.default_rng(1))
+        assert kp.shape[2] == P
+        outs.append(attention.paged_decode_attention(q, kp, vp, tab, np.array(ctxs), 0.2, "f16", "f16"))
+    np.testing.assert_array_equal(outs[0], outs[1])

@@ -9,7 +9,7 @@ cache per §5.2). Block size 16 throughout (§2.2 of the same page).
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 
 @dataclass(frozen=True)
@@ -93,4 +93,13 @@ PREFILL_70B_GQA = WorkloadConfig(
                 "prefixes of 0-3584 tokens (ctx U[512,4096]), 64 q / 8 kv heads, D 128, bf16")
 
 PREFILL_CONFIGS = {c.name: c for c in (PREFILL_TINY, PREFILL_70B_GQA)}
-ALL_CONFIGS = {**CONFIGS, **PREFILL_CONFIGS}
+
+# The block-size question of "vLLM 推理优化技术深度调研报告", 维度四.5 (bigger pages: fewer
+# table entries, more internal fragmentation): the Llama-2-70B GQA decode layer with
+# 32- and 64-token blocks, the same seed (the same contexts) and the same pool bytes.
+LLAMA2_70B_GQA_P32 = replace(LLAMA2_70B_GQA, name="llama2_70b_gqa_p32", block_size=32, num_blocks=8192,
+                             description="Llama-2-70B GQA layer with 32-token blocks (else as llama2_70b_gqa)")
+LLAMA2_70B_GQA_P64 = replace(LLAMA2_70B_GQA, name="llama2_70b_gqa_p64", block_size=64, num_blocks=4096,
+                             description="Llama-2-70B GQA layer with 64-token blocks (else as llama2_70b_gqa)")
+BLOCK_SIZE_CONFIGS = {c.name: c for c in (LLAMA2_70B_GQA_P32, LLAMA2_70B_GQA_P64)}
+ALL_CONFIGS = {**CONFIGS, **PREFILL_CONFIGS, **BLOCK_SIZE_CONFIGS}
