@@ -97,6 +97,7 @@ struct PrefillTraits {
 template <int QT, int KVT, int D>
 __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(const PrefillArgs a) {
   using Tr = PrefillTraits<KVT, D>;
+  constexpr int NCB = kPrefillCols / 16;   // 16-column MFMA blocks per wavefront
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][Tr::kKTile + Tr::kVTile];   // [buffer]: K tile, V tile
   __shared__ __attribute__((aligned(16))) int ids_lds[kIdsRing];
 
@@ -128,10 +129,10 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
 
   // ---- this wavefront's rows: Q^T operands and causal limits ------------------------------
   const int wrow0 = row0 + w * kPrefillCols;
-  u32x4 qb[2][D / 32];
-  int limit[2];
+  u32x4 qb[NCB][D / 32];
+  int limit[NCB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
     const int r = wrow0 + cb * 16 + n16;
     const bool valid = r < R;
     const int tok = valid ? r / G : 0, h = valid ? r % G : 0;
@@ -218,10 +219,10 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
   };
 
   // ---- running softmax state: per lane, column n16 of each block, rows 4j4.. of each d-tile
-  f32x4 o[2][D / 16];
-  float m[2], l[2];
+  f32x4 o[NCB][D / 16];
+  float m[NCB], l[NCB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) o[cb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[cb] = -INFINITY;
@@ -234,37 +235,48 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
   const int k_lane = n16 * Tr::kKRow + j4 * 16;
   const int v_lane = (4 * j4 + (n16 >> 2)) * Tr::kVRow + (n16 & 3) * 8;
 
+  // Per tile: all of QK^T, then the causal select, then each column's new reference
+  // maximum (one branch for the rare rescale), then the exponentials of the first 32 keys,
+  // the PV products of the first 32 keys (independent of the exponentials of the last 32,
+  // so the two can overlap in one straight-line block), and the last 32 keys.
   auto compute = [&](int i, int buf) {
     const uint8_t* kl = lds[buf] + k_lane;
     const uint8_t* vl = lds[buf] + Tr::kKTile + v_lane;
     const int k0 = i * kPrefillKeys;
-    // S^T = K . Q^T for the four 16-key tiles.
-    f32x4 sc[4][2];
+    // S^T = K . Q^T for the four 16-key tiles. A wavefront in a matrix-core phase runs at
+    // a raised issue priority, so the two wavefronts of a SIMD drift into complementary
+    // phases (one multiplying while the other computes exponentials).
+    __builtin_amdgcn_s_setprio(1);
+    f32x4 sc[4][NCB];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      sc[kt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sc[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) sc[kt][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
         const u32x4 ka = *(const u32x4*)(kl + kt * 16 * Tr::kKRow + c * 64);   // elements 32c + 8j4 .. + 7
-        sc[kt][0] = mfma16x16x32<QT>(ka, qb[0][c], sc[kt][0]);
-        sc[kt][1] = mfma16x16x32<QT>(ka, qb[1][c], sc[kt][1]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) sc[kt][cb] = mfma16x16x32<QT>(ka, qb[cb][c], sc[kt][cb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // Causal limits (and keys past the workgroup's last one) on tiles that reach them.
     if (k0 + kPrefillKeys > wave_lo) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (k0 + kt * 16 + 4 * j4 + e >= limit[cb]) sc[kt][cb][e] = -INFINITY;
     }
-    // Online softmax per column block; P^T packed as the B operands of the PV steps.
-    u32x4 pb[2][2];   // [32-key half][column block]
+    // Lazy rescaling: the reference point m of a column moves only when a score exceeds it
+    // by more than kLazyRescale (log2 units), so weights stay below 2^8 and the
+    // accumulators are rescaled rarely. Any reference gives the same quotient.
+    float m_ref[NCB], alpha[NCB];
+    bool rescale = false;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       // (scores are never NaN here: stale rows were replaced by -inf above)
       const float m0 = max3_nn(sc[0][cb][0], sc[0][cb][1], sc[0][cb][2]);
       const float m1 = max3_nn(sc[0][cb][3], sc[1][cb][0], sc[1][cb][1]);
@@ -273,37 +285,39 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
       const float m4 = max3_nn(sc[3][cb][0], sc[3][cb][1], sc[3][cb][2]);
       float mx = max_nn(max3_nn(m0, m1, m2), max3_nn(m3, m4, sc[3][cb][3]));
       mx = max_nn_xor32(max_nn_xor16(mx)) * qk_scale;    // the scale is positive
-      // Lazy rescaling: the reference point m of a column moves only when a score
-      // exceeds it by more than kLazyRescale (log2 units), so weights stay below 2^8 and
-      // the accumulators are rescaled rarely. Any reference gives the same quotient.
       const float m_new = mx > m[cb] + kLazyRescale ? mx : m[cb];
-      const float alpha = m[cb] == m_new ? 1.0f : exp2_fast(m[cb] - m_new);   // exp2(-inf) = 0
+      alpha[cb] = m[cb] == m_new ? 1.0f : exp2_fast(m[cb] - m_new);   // exp2(-inf) = 0
+      rescale = rescale || alpha[cb] != 1.0f;
       m[cb] = m_new;
       // A column that has seen no live key keeps m = -inf; exponents are then taken
       // against 0 so that they come out as exp2(-inf) = 0, never as exp2(-inf + inf).
-      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-      uint32_t pk[4][2];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        pk[kt][0] = pack2<QT>(exp2_fast(fmaf(sc[kt][cb][0], qk_scale, -m_ref)),
-                              exp2_fast(fmaf(sc[kt][cb][1], qk_scale, -m_ref)));
-        pk[kt][1] = pack2<QT>(exp2_fast(fmaf(sc[kt][cb][2], qk_scale, -m_ref)),
-                              exp2_fast(fmaf(sc[kt][cb][3], qk_scale, -m_ref)));
-      }
-      if (__any(alpha != 1.0f)) {
-        l[cb] *= alpha;
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) o[cb][c] *= alpha;
-      }
-      // The denominator sums the rounded weights that the PV product uses.
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) l[cb] = dot2_ones<QT>(pk[kt][1], dot2_ones<QT>(pk[kt][0], l[cb]));
-      pb[0][cb] = u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
-      pb[1][cb] = u32x4{pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
+      m_ref[cb] = m_new == -INFINITY ? 0.f : m_new;
     }
-    // O^T += V^T . P^T, 32 keys per step.
+    if (__any(rescale)) {
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+      for (int cb = 0; cb < NCB; ++cb) {
+        l[cb] *= alpha[cb];
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) o[cb][c] *= alpha[cb];
+      }
+    }
+    // P^T of 32 keys (16-key tiles 2hf, 2hf + 1) as the B operands of one PV step; the
+    // denominator sums the rounded weights that the PV product uses.
+    auto weights = [&](int hf, u32x4* pb) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const f32x4 a = sc[2 * hf][cb], b = sc[2 * hf + 1][cb];
+        const float r = m_ref[cb];
+        const uint32_t p0 = pack2<QT>(exp2_fast(fmaf(a[0], qk_scale, -r)), exp2_fast(fmaf(a[1], qk_scale, -r)));
+        const uint32_t p1 = pack2<QT>(exp2_fast(fmaf(a[2], qk_scale, -r)), exp2_fast(fmaf(a[3], qk_scale, -r)));
+        const uint32_t p2 = pack2<QT>(exp2_fast(fmaf(b[0], qk_scale, -r)), exp2_fast(fmaf(b[1], qk_scale, -r)));
+        const uint32_t p3 = pack2<QT>(exp2_fast(fmaf(b[2], qk_scale, -r)), exp2_fast(fmaf(b[3], qk_scale, -r)));
+        l[cb] = dot2_ones<QT>(p3, dot2_ones<QT>(p2, dot2_ones<QT>(p1, dot2_ones<QT>(p0, l[cb]))));
+        pb[cb] = u32x4{p0, p1, p2, p3};
+      }
+    };
+    // O^T += V^T . P^T over the 32 keys of step hf.
+    auto pv = [&](int hf, const u32x4* pb) {
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         const uint8_t* va_p = vl + hf * 32 * Tr::kVRow + c * 32;
@@ -312,10 +326,19 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
             (__attribute__((address_space(3))) i16x4*)(va_p + 16 * Tr::kVRow));
         const u32x2 wa = __builtin_bit_cast(u32x2, va), wb = __builtin_bit_cast(u32x2, vb);
         const u32x4 av = {wa[0], wa[1], wb[0], wb[1]};
-        o[0][c] = mfma16x16x32<QT>(av, pb[hf][0], o[0][c]);
-        o[1][c] = mfma16x16x32<QT>(av, pb[hf][1], o[1][c]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) o[cb][c] = mfma16x16x32<QT>(av, pb[cb], o[cb][c]);
       }
-    }
+    };
+    u32x4 pb0[NCB], pb1[NCB];
+    weights(0, pb0);
+    __builtin_amdgcn_s_setprio(1);
+    pv(0, pb0);
+    __builtin_amdgcn_s_setprio(0);
+    weights(1, pb1);
+    __builtin_amdgcn_s_setprio(1);
+    pv(1, pb1);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- main loop: one tile in LDS, the next two in flight ------------------------------
@@ -348,7 +371,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
 
   // ---- results ----------------------------------------------------------------------------
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
     const float l_tot = sum_xor32(sum_xor16(l[cb]));
     const int r = wrow0 + cb * 16 + n16;
     if (r < R) {
