@@ -41,9 +41,16 @@ DECODE_SOURCES = ("paged_kv_cache_409_amd/csrc/decode_mfma.hip", "paged_kv_cache
                   "paged_kv_cache_409_amd/csrc/decode_common.h", "paged_kv_cache_409_amd/csrc/pkv_device.h")
 
 
-PREFILL_SOURCES = ("paged_kv_cache_409_amd/csrc/prefill_mfma.hip", "paged_kv_cache_409_amd/csrc/decode_common.h",
-                   "paged_kv_cache_409_amd/csrc/pkv_device.h", "paged_kv_cache_409_amd/csrc/pkv_launch.h",
-                   "paged_kv_cache_409_amd/build.py")
+PREFILL_COMMON = ("paged_kv_cache_409_amd/csrc/prefill_common.h", "paged_kv_cache_409_amd/csrc/decode_common.h",
+                  "paged_kv_cache_409_amd/csrc/pkv_device.h", "paged_kv_cache_409_amd/csrc/pkv_launch.h",
+                  "paged_kv_cache_409_amd/build.py")
+
+
+def prefill_kernel(kv_dtype: str):
+    """(kernel name, sources) of the prefill kernel that serves a cache of this dtype."""
+    if kv_dtype == "fp8_e4m3":
+        return "paged_prefill_mfma", ("paged_kv_cache_409_amd/csrc/prefill_mfma.hip",) + PREFILL_COMMON
+    return "paged_prefill_lds", ("paged_kv_cache_409_amd/csrc/prefill_lds.hip",) + PREFILL_COMMON
 
 
 def kernel_source_hash(sources=DECODE_SOURCES) -> str:
@@ -259,6 +266,7 @@ def prefill_bench(args, cfg, dev) -> int:
     pf_avg_ms = float(pf_ms.mean())
     ev_flops = sum(flops_r[(first + i) % len(batches)] for i in range(args.steps))
     achieved = ev_flops / (float(pf_ms.sum()) * 1e-3) / 1e12
+    kernel, sources = prefill_kernel(cfg.kv_dtype)
     result = {
         "metric": "paged prefill-chunk attention: achieved matrix TFLOP/s (% of dense bf16 peak) and tokens/s",
         "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 1),
@@ -287,8 +295,8 @@ def prefill_bench(args, cfg, dev) -> int:
                        "p90": round(float(np.percentile(pf_ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": load_traffic(cfg.name, "prefill", PREFILL_SOURCES),
-                     "kernel": "paged_prefill_mfma", "kernel_source_hash": kernel_source_hash(PREFILL_SOURCES)},
+                     "traffic": load_traffic(cfg.name, "prefill", sources),
+                     "kernel": kernel, "kernel_source_hash": kernel_source_hash(sources)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

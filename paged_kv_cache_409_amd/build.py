@@ -32,7 +32,7 @@ COMMON = [
 # Extra flags of single sources. The prefill kernel lets no NaN reach a maximum or an
 # exponent, so it is built with relaxed NaN handling: its score maxima then skip the
 # NaN-quieting of matrix-core results (about a tenth of its vector instructions).
-FILE_FLAGS = {"prefill_mfma.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {"prefill_mfma.hip": ["-fno-honor-nans"], "prefill_lds.hip": ["-fno-honor-nans"]}
 
 
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -356,6 +356,9 @@ int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache, c
   a.v_scale = fp8 ? v_scale : 1.0f;
   const int qt = q_dtype == PKV_BF16 ? pkv::kBF16 : pkv::kF16;
   const int kt = fp8 ? pkv::kFP8 : qt;
+  // A 16-bit cache goes to the kernel that loads K/V straight into LDS; an fp8 cache is
+  // widened on the way through registers.
+  if (!fp8) return hip_status(pkv::launch_prefill_lds(a, qt, head_dim, reinterpret_cast<hipStream_t>(stream)));
   return hip_status(pkv::launch_prefill_mfma(a, qt, kt, head_dim, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -71,14 +71,16 @@ struct PrefillArgs {
   float v_scale;                  // 1, or v_scale for an fp8 cache
 };
 
-// Prefill workgroup: 4 wavefronts x 32 query rows, keys taken 64 (four cache blocks) at
-// a time.
+// Prefill workgroup: 4 wavefronts x 32 query rows. The fp8-cache kernel takes keys 64
+// (four 16-token tiles) at a time through registers; the 16-bit-cache kernel takes 32 at
+// a time straight into LDS.
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillCols = 32;
 constexpr int kPrefillRows = kPrefillWaves * kPrefillCols;
 constexpr int kPrefillKeys = 64;
 
-hipError_t launch_prefill_mfma(const PrefillArgs& a, int q_type, int kv_type, int head_dim, hipStream_t s);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int q_type, int kv_type, int head_dim, hipStream_t s);   // fp8 cache
+hipError_t launch_prefill_lds(const PrefillArgs& a, int q_type, int head_dim, hipStream_t s);                 // 16-bit cache
 hipError_t launch_decode_mfma(const DecodeArgs& a, int q_type, int kv_type, int head_dim, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, int q_type, int kv_type, int head_dim, hipStream_t s);
 hipError_t launch_decode_reduce(const ReduceArgs& a, int q_type, int head_dim, hipStream_t s);

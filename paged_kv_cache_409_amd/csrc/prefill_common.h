@@ -1,0 +1,49 @@
+// Pieces shared by the two prefill-chunk kernels (register-staged and direct-to-LDS).
+// Both files that include this are compiled with -fno-honor-nans (see max_nn below).
+#pragma once
+
+#include "pkv_launch.h"
+
+namespace pkv {
+
+template <int QT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (QT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// acc + lo + hi of two packed 16-bit values (one v_dot2 against (1, 1)).
+template <int QT>
+__device__ __forceinline__ float dot2_ones(uint32_t p, float acc) {
+  if constexpr (QT == kBF16) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
+  } else {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), one, acc, false);
+  }
+}
+
+constexpr float kLazyRescale = 8.0f;
+constexpr int kIdsRing = 1024;   // block-table entries a workgroup keeps in LDS
+
+// Maxima of scores. The prefill files are compiled with -fno-honor-nans: no score that reaches a
+// maximum or an exponent is NaN (stale rows are replaced by -inf through a select on an
+// integer condition first), so IEEE max needs no NaN-quieting of operands that come
+// straight from the matrix cores, and chains of maxima become v_max3.
+__device__ __forceinline__ float max_nn(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ float max3_nn(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+__device__ __forceinline__ float max_nn_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_nn_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+}  // namespace pkv

@@ -1,4 +1,6 @@
-// Paged attention of prefill chunks on gfx950 matrix cores.
+// Paged attention of prefill chunks on gfx950 matrix cores, over an fp8 cache (a 16-bit
+// cache is served by the direct-to-LDS kernel in prefill_lds.hip, whose tiles go to LDS
+// unchanged; here every tile passes through registers to be widened).
 //
 // The method (what is computed): long prompts are cut into chunks that run between
 // decode steps ("vLLM推理引擎PagedAttention原理与性能优化实战", §六). A chunk of n new
@@ -26,59 +28,20 @@
 //   each row is applied by select only on tiles that reach past the wavefront's first
 //   row's limit; a wavefront skips tiles wholly past its last row;
 // * V rows past the workgroup's last key are zeroed when staged (0 * stale NaN would
-//   poison the product); an fp8 (OCP E4M3FN) cache is widened exactly to the q dtype as
+//   poison the product); the fp8 (OCP E4M3FN) cache is widened exactly to the q dtype as
 //   it is staged, its per-tensor scales folded into the logit and output scales;
 // * work items are ordered kv head, sequence, row tile (last rows first: they see the
 //   most keys), and each XCD takes a contiguous range of them, so the row tiles of one
 //   (sequence, kv head) run on one XCD and re-read its K/V from that XCD's L2.
-#include "pkv_launch.h"
+#include "prefill_common.h"
 
 namespace pkv {
 
-template <int QT>
-__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
-  if constexpr (QT == kBF16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-// acc + lo + hi of two packed 16-bit values (one v_dot2 against (1, 1)).
-template <int QT>
-__device__ __forceinline__ float dot2_ones(uint32_t p, float acc) {
-  if constexpr (QT == kBF16) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
-  } else {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), one, acc, false);
-  }
-}
-
-constexpr float kLazyRescale = 8.0f;
-constexpr int kIdsRing = 1024;   // block-table entries a workgroup keeps in LDS
-
-// Maxima of scores. This file is compiled with -fno-honor-nans: no score that reaches a
-// maximum or an exponent is NaN (stale rows are replaced by -inf through a select on an
-// integer condition first), so IEEE max needs no NaN-quieting of operands that come
-// straight from the matrix cores, and chains of maxima become v_max3.
-__device__ __forceinline__ float max_nn(float a, float b) { return fmaxf(a, b); }
-__device__ __forceinline__ float max3_nn(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
-__device__ __forceinline__ float max_nn_xor16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_nn_xor32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
 template <int KVT, int D>
 struct PrefillTraits {
+  static_assert(KVT == kFP8, "16-bit caches use the direct-to-LDS kernel");
   static constexpr int kThreads = kWave * kPrefillWaves;
-  static constexpr int kElem = (KVT == kFP8) ? 1 : 2;              // bytes per cache element
+  static constexpr int kElem = 1;                                  // bytes per cache element
   static constexpr int kBlockBytes = kBlock * D * kElem;           // one kv head's slice of a 16-token tile
   static constexpr int kChunksPerBlock = kBlockBytes / 16;
   static constexpr int kLoads = kPrefillKeys * D * kElem / 16 / kThreads;  // per thread, K (or V)
@@ -196,7 +159,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
     for (int u = 0; u < Tr::kLoads; ++u) {
       const int f = u * Tr::kThreads + t;
       const int j = f / Tr::kChunksPerBlock, c = f % Tr::kChunksPerBlock;
-      if constexpr (KVT == kFP8) {
+      {
         const int r = j * kBlock + c / (D / 16), ch = c % (D / 16);   // 16 codes = 2 LDS chunks
         const u32x4 wk = rk[u];
         const u32x4 wv = i * kPrefillKeys + r < kv_end ? rv[u] : u32x4{0u, 0u, 0u, 0u};
@@ -210,10 +173,6 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
         *(u32x4*)(kd + 16) = u32x4{k2[0], k2[1], k3[0], k3[1]};
         *(u32x4*)(vd) = u32x4{v0[0], v0[1], v1[0], v1[1]};
         *(u32x4*)(vd + 16) = u32x4{v2[0], v2[1], v3[0], v3[1]};
-      } else {
-        const int r = j * kBlock + c / (D / 8), ch = c % (D / 8);
-        *(u32x4*)(kl + r * Tr::kKRow + ch * 16) = rk[u];
-        *(u32x4*)(vl + r * Tr::kVRow + ch * 16) = i * kPrefillKeys + r < kv_end ? rv[u] : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -397,8 +356,6 @@ static hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int q_type, int kv_type, int head_dim, hipStream_t stream) {
 #define PKV_CASE(QT, KVT, D) \
   if (q_type == QT && kv_type == KVT && head_dim == D) return launch_t<QT, KVT, D>(a, stream);
-  PKV_CASE(kBF16, kBF16, 128) PKV_CASE(kBF16, kBF16, 64)
-  PKV_CASE(kF16, kF16, 128) PKV_CASE(kF16, kF16, 64)
   PKV_CASE(kBF16, kFP8, 128) PKV_CASE(kBF16, kFP8, 64)
   PKV_CASE(kF16, kFP8, 128) PKV_CASE(kF16, kFP8, 64)
 #undef PKV_CASE
