@@ -48,9 +48,9 @@ __device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, lds_ptr
 constexpr int kLdsKeys = 32;    // keys per LDS stage (two 16-token tiles)
 constexpr int kLdsStages = 3;
 
-template <int D>
+template <int D, int W>
 struct LdsTraits {
-  static constexpr int kThreads = kWave * kPrefillWaves;
+  static constexpr int kThreads = kWave * W;
   static constexpr int kRow = D * 2;                         // bytes of one 16-bit row
   static constexpr int kRowChunks = D / 8;                   // 16-byte chunks per row
   static constexpr int kTile16 = kBlock * kRow;              // one kv head's slice of a 16-token tile
@@ -71,9 +71,10 @@ __device__ __forceinline__ int v_swz(int r) {
   return RC >= 16 ? ((2 * (r & 3)) ^ (8 * ((r >> 2) & 1))) : 2 * (r & 3);
 }
 
-template <int QT, int D>
-__global__ __launch_bounds__(kWave * kPrefillWaves, 3) void paged_prefill_lds(const PrefillArgs a) {
-  using Tr = LdsTraits<D>;
+template <int QT, int D, int W>
+__global__ __launch_bounds__(kWave * W, 3) void paged_prefill_lds(const PrefillArgs a) {
+  using Tr = LdsTraits<D, W>;
+  constexpr int kRows = W * kPrefillCols;   // query rows of a workgroup
   constexpr int RC = Tr::kRowChunks;
   constexpr int NCB = kPrefillCols / 16;
   constexpr int kStageBytes = 2 * Tr::kStageTile;
@@ -102,15 +103,15 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 3) void paged_prefill_lds(co
   if (q0 < 0 || q1 < q0 || q1 > a.num_tokens) return;
   const int n = min(min(q1 - q0, a.max_query_len), ctx);
   const int R = n * G;
-  const int row0 = tile * kPrefillRows;
+  const int row0 = tile * kRows;
   if (row0 >= R) return;
   const int prefix = ctx - n;
-  const int kv_end = prefix + (min(R, row0 + kPrefillRows) - 1) / G + 1;
+  const int kv_end = prefix + (min(R, row0 + kRows) - 1) / G + 1;
   const int ntiles = (kv_end + kBlock - 1) / kBlock;
   const int n_iter = (kv_end + kLdsKeys - 1) / kLdsKeys;
 
   const int t = threadIdx.x, w = readfirstlane(t / kWave), lane = t & (kWave - 1);
-  __builtin_assume(w >= 0 && w < kPrefillWaves);
+  __builtin_assume(w >= 0 && w < W);
   const int n16 = lane & 15, j4 = lane >> 4;
 
   // ---- this wavefront's rows ---------------------------------------------------------------
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 3) void paged_prefill_lds(co
   int rrow[Tr::kLoads];
 #pragma unroll
   for (int u = 0; u < Tr::kLoads; ++u) {
-    const int o = (u * kPrefillWaves + w) * 1024 + lane * 16;
+    const int o = (u * W + w) * 1024 + lane * 16;
     const int rr = o / Tr::kRow, pc = (o % Tr::kRow) / 16;
     rrow[u] = rr;
     koff[u] = (uint32_t)((rr % kBlock) * Tr::kRow + (pc ^ k_swz<RC>(rr)) * 16);
@@ -161,14 +162,14 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 3) void paged_prefill_lds(co
     uint8_t* st = stage(stg);
 #pragma unroll
     for (int u = 0; u < Tr::kLoads; ++u) {
-      const int sub = ((u * kPrefillWaves + w) * 1024) / Tr::kRow / kBlock;   // 16-token tile of this instruction
+      const int sub = ((u * W + w) * 1024) / Tr::kRow / kBlock;   // 16-token tile of this instruction
       const int id = readfirstlane((int)(sub == 0 ? ids[0] : ids[1]));
       const bool live = id >= 0;
       const int64_t off = live ? tile_offset(id, shift, block_stride, Tr::kTile16) : 0;
       const uint32_t bytes = live ? (uint32_t)Tr::kTile16 : 0u;
       // rows past the workgroup's last key load as zeros (offset past the buffer)
       const bool row_live = i * kLdsKeys + rrow[u] < kv_end;
-      uint8_t* dk = st + (u * kPrefillWaves + w) * 1024;
+      uint8_t* dk = st + (u * W + w) * 1024;
       buf_load_lds16(make_rsrc(kbase + off, bytes), (lds_ptr)dk, row_live ? koff[u] : 0x80000000u);
       buf_load_lds16(make_rsrc(vbase + off, bytes), (lds_ptr)(dk + Tr::kStageTile), row_live ? voff[u] : 0x80000000u);
     }
@@ -344,10 +345,15 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 3) void paged_prefill_lds(co
   __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Four wavefronts (128 query rows, the host's row tiles) per workgroup, three workgroups
+// per CU. (Eight wavefronts share each tile among twice the rows but leave room for only
+// two wavefronts per SIMD, which measured slower.)
 template <int QT, int D>
 static hipError_t launch_lds(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int W = kPrefillWaves;
+  static_assert(W * kPrefillCols == kPrefillRows, "row tiles as the host counts them");
   const int grid = (a.num_items + 7) / 8 * 8;
-  hipLaunchKernelGGL((paged_prefill_lds<QT, D>), dim3(grid), dim3(kWave * kPrefillWaves), 0, stream, a);
+  hipLaunchKernelGGL((paged_prefill_lds<QT, D, W>), dim3(grid), dim3(kWave * W), 0, stream, a);
   return hipGetLastError();
 }
 

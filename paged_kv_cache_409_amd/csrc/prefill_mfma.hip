@@ -178,13 +178,17 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
   };
 
   // ---- running softmax state: per lane, column n16 of each block, rows 4j4.. of each d-tile
+  // m: a row's reference point (log2 units), m_ref: the one exponents are taken against
+  // (0 while m = -inf), m_bound = m + kLazyRescale.
   f32x4 o[NCB][D / 16];
-  float m[NCB], l[NCB];
+  float m[NCB], m_ref[NCB], m_bound[NCB], l[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) o[cb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[cb] = -INFINITY;
+    m_ref[cb] = 0.f;
+    m_bound[cb] = -INFINITY;
     l[cb] = 0.f;
   }
   const float qk_scale = a.qk_scale_log2;
@@ -231,9 +235,12 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
     }
     // Lazy rescaling: the reference point m of a column moves only when a score exceeds it
     // by more than kLazyRescale (log2 units), so weights stay below 2^8 and the
-    // accumulators are rescaled rarely. Any reference gives the same quotient.
-    float m_ref[NCB], alpha[NCB];
-    bool rescale = false;
+    // accumulators are rescaled rarely. Any reference gives the same quotient. Each lane
+    // tests its own sixteen scores of the column; only a wavefront where some test fires
+    // takes the column maxima across lanes and rescales (columns whose reference stays
+    // put get a factor of 1).
+    float lmax[NCB];
+    bool over = false;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       // (scores are never NaN here: stale rows were replaced by -inf above)
@@ -242,22 +249,23 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
       const float m2 = max3_nn(sc[1][cb][2], sc[1][cb][3], sc[2][cb][0]);
       const float m3 = max3_nn(sc[2][cb][1], sc[2][cb][2], sc[2][cb][3]);
       const float m4 = max3_nn(sc[3][cb][0], sc[3][cb][1], sc[3][cb][2]);
-      float mx = max_nn(max3_nn(m0, m1, m2), max3_nn(m3, m4, sc[3][cb][3]));
-      mx = max_nn_xor32(max_nn_xor16(mx)) * qk_scale;    // the scale is positive
-      const float m_new = mx > m[cb] + kLazyRescale ? mx : m[cb];
-      alpha[cb] = m[cb] == m_new ? 1.0f : exp2_fast(m[cb] - m_new);   // exp2(-inf) = 0
-      rescale = rescale || alpha[cb] != 1.0f;
-      m[cb] = m_new;
-      // A column that has seen no live key keeps m = -inf; exponents are then taken
-      // against 0 so that they come out as exp2(-inf) = 0, never as exp2(-inf + inf).
-      m_ref[cb] = m_new == -INFINITY ? 0.f : m_new;
+      lmax[cb] = max_nn(max3_nn(m0, m1, m2), max3_nn(m3, m4, sc[3][cb][3]));
+      over = over || lmax[cb] * qk_scale > m_bound[cb];   // the scale is positive
     }
-    if (__any(rescale)) {
+    if (__any(over)) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        l[cb] *= alpha[cb];
+        const float mx = max_nn_xor32(max_nn_xor16(lmax[cb])) * qk_scale;
+        const float m_new = mx > m_bound[cb] ? mx : m[cb];
+        const float alpha = m[cb] == m_new ? 1.0f : exp2_fast(m[cb] - m_new);   // exp2(-inf) = 0
+        m[cb] = m_new;
+        // A column that has seen no live key keeps m = -inf; exponents are then taken
+        // against 0 so that they come out as exp2(-inf) = 0, never as exp2(-inf + inf).
+        m_ref[cb] = m_new == -INFINITY ? 0.f : m_new;
+        m_bound[cb] = m_new + kLazyRescale;
+        l[cb] *= alpha;
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) o[cb][c] *= alpha[cb];
+        for (int c = 0; c < D / 16; ++c) o[cb][c] *= alpha;
       }
     }
     // P^T of 32 keys (16-key tiles 2hf, 2hf + 1) as the B operands of one PV step; the
