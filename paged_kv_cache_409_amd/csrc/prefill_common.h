@@ -31,6 +31,39 @@ __device__ __forceinline__ float dot2_ones(uint32_t p, float acc) {
 constexpr float kLazyRescale = 8.0f;
 constexpr int kIdsRing = 1024;   // block-table entries a workgroup keeps in LDS
 
+// Work items visit sequences longest first: the sequence of rank r in decreasing order of
+// work n (2 ctx - n) (new tokens times twice the mean context they attend to; ties by
+// index), so the longest items start first and the short ones fill the tail. Every
+// workgroup computes the same order; with more than kSortSeqs sequences the order is the
+// batch's own. `scratch` is LDS of at least kSortSeqs + 1 ints, free on entry and on return.
+constexpr int kSortSeqs = 256;
+__device__ __forceinline__ int seq_of_rank(const PrefillArgs& a, int r, int* scratch) {
+  const int S = a.num_seqs;
+  if (S > kSortSeqs) return r;
+  float* work = reinterpret_cast<float*>(scratch);
+  for (int t = threadIdx.x; t < S; t += blockDim.x) {
+    const int q0 = a.query_start_loc[t], q1 = a.query_start_loc[t + 1];
+    const int ctx = min(max(a.context_lens[t], 0), (a.max_blocks * kBlock) << a.block_shift);
+    const bool ok = q0 >= 0 && q1 >= q0 && q1 <= a.num_tokens;
+    const int n = ok ? min(min(q1 - q0, a.max_query_len), ctx) : 0;
+    work[t] = (float)n * (float)(2 * ctx - n);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < S; t += blockDim.x) {
+    const float wt = work[t];
+    int rank = 0;
+    for (int u = 0; u < S; ++u) {
+      const float wu = work[u];
+      rank += (wu > wt || (wu == wt && u < t)) ? 1 : 0;
+    }
+    if (rank == r) scratch[kSortSeqs] = t;   // ranks are a permutation: exactly one writer
+  }
+  __syncthreads();
+  const int s = scratch[kSortSeqs];
+  __syncthreads();
+  return s;
+}
+
 // Maxima of scores. The prefill files are compiled with -fno-honor-nans: no score that reaches a
 // maximum or an exponent is NaN (stale rows are replaced by -inf through a select on an
 // integer condition first), so IEEE max needs no NaN-quieting of operands that come

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kWave * W, 3) void paged_prefill_lds(const PrefillA
   if (item >= a.num_items) return;
   const int pair = item / a.row_tiles;
   const int tile = a.row_tiles - 1 - item % a.row_tiles;
-  const int g = pair / a.num_seqs, s = pair % a.num_seqs;
+  const int g = pair / a.num_seqs, s = seq_of_rank(a, pair % a.num_seqs, ids_lds);
   const int G = a.group;
   const int shift = a.block_shift;
   const int ctx = min(max(a.context_lens[s], 0), (a.max_blocks * kBlock) << shift);

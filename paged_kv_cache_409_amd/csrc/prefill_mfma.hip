@@ -30,9 +30,10 @@
 // * V rows past the workgroup's last key are zeroed when staged (0 * stale NaN would
 //   poison the product); the fp8 (OCP E4M3FN) cache is widened exactly to the q dtype as
 //   it is staged, its per-tensor scales folded into the logit and output scales;
-// * work items are ordered kv head, sequence, row tile (last rows first: they see the
-//   most keys), and each XCD takes a contiguous range of them, so the row tiles of one
-//   (sequence, kv head) run on one XCD and re-read its K/V from that XCD's L2.
+// * work items are ordered kv head, sequence (the most work first), row tile (last rows
+//   first: they see the most keys), and each XCD takes a contiguous range of them, so the
+//   row tiles of one (sequence, kv head) run on one XCD and re-read its K/V from that
+//   XCD's L2, and the longest items start first.
 #include "prefill_common.h"
 
 namespace pkv {
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
   if (item >= a.num_items) return;
   const int pair = item / a.row_tiles;
   const int tile = a.row_tiles - 1 - item % a.row_tiles;
-  const int g = pair / a.num_seqs, s = pair % a.num_seqs;
+  const int g = pair / a.num_seqs, s = seq_of_rank(a, pair % a.num_seqs, ids_lds);
   const int G = a.group;
 
   const int shift = a.block_shift;   // a cache block holds kBlock << shift tokens, walked in kBlock-token tiles

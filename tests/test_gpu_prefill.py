@@ -52,6 +52,19 @@ def test_whole_prompts_at_tile_edges(G, dtype, kv_dtype):
     assert (np.diff(h.query_start_loc) == h.context_lens).all()
 
 
+@pytest.mark.parametrize("S", [7, 256, 257])
+@pytest.mark.parametrize("dtype,kv_dtype", [("bf16", "bf16"), ("bf16", "fp8_e4m3")])
+def test_many_sequences_in_any_order(S, dtype, kv_dtype):
+    # Workgroups visit sequences by decreasing work for up to 256 sequences and in batch
+    # order beyond that; equal-work sequences (ties) and empty chunks included.
+    rng = np.random.default_rng(S)
+    ctx = rng.integers(1, 120, size=S)
+    ctx[: S // 3] = 64                                        # ties
+    cfg = prefill_cfg(4, 64, dtype, kv_dtype, S=S, Hkv=1, ctx=("fixed", ctx.tolist()), chunk=("uniform", 0, 40),
+                      max_ctx=120, seed=S)
+    _case(cfg)
+
+
 @pytest.mark.parametrize("G,dtype,kv_dtype", [(8, "bf16", "bf16"), (2, "f16", "fp8_e4m3")])
 def test_one_token_chunks_are_decode_steps(G, dtype, kv_dtype):
     _case(prefill_cfg(G, 128, dtype, kv_dtype, S=12, ctx=("uniform", 1, 700), chunk=("fixed", 1), max_ctx=700))
