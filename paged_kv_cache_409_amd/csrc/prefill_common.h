@@ -46,7 +46,7 @@ __device__ __forceinline__ int seq_of_rank(const PrefillArgs& a, int r, int* scr
     const int ctx = min(max(a.context_lens[t], 0), (a.max_blocks * kBlock) << a.block_shift);
     const bool ok = q0 >= 0 && q1 >= q0 && q1 <= a.num_tokens;
     const int n = ok ? min(min(q1 - q0, a.max_query_len), ctx) : 0;
-    work[t] = (float)n * (float)(2 * ctx - n);
+    work[t] = (float)n * (2.0f * (float)ctx - (float)n);   // in float: 2 ctx may exceed int
   }
   __syncthreads();
   for (int t = threadIdx.x; t < S; t += blockDim.x) {
