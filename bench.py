@@ -114,9 +114,10 @@ def main() -> int:
     cfg = {**CONFIGS, **BLOCK_SIZE_CONFIGS}[args.config]
     batches = [make_batch(cfg, dev, replica=r) for r in range(args.replicas)]
     lay = batches[0].layout
-    kv_logical = kv_bytes_logical(cfg, lay.context_lens)
-    kv_unique = kv_bytes_unique(cfg, lay)
-    kv_alg = kv_unique                        # distinct bytes a step must read (= logical unless blocks are shared)
+    # Replicas draw their own context lengths: each step counts the bytes of its own batch.
+    # Algorithmic bytes are the distinct bytes a step must read (= logical unless blocks are shared).
+    kv_alg_r = [kv_bytes_unique(cfg, b.layout) for b in batches]
+    kv_log_r = [kv_bytes_logical(cfg, b.layout.context_lens) for b in batches]
     ws_bytes = pkv.workspace_size(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                                   cfg.max_context_len, cfg.partition_size)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
@@ -155,6 +156,7 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    step_bytes = sum(kv_alg_r[(args.warmup + i) % len(batches)] for i in range(args.steps)) / args.steps
     # Second pass, for the roofline: the same steps with the decode launch bracketed by
     # events on its stream (per-launch events cost GPU time, so they stay out of the
     # timed region above).
@@ -164,11 +166,18 @@ def main() -> int:
     torch.cuda.synchronize()
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
     dec_avg_ms = float(dec_ms.mean())
-    achieved = kv_alg / (dec_avg_ms * 1e-3) / 1e9
+    first = args.warmup + args.steps
+    ev_bytes = sum(kv_alg_r[(first + i) % len(batches)] for i in range(args.steps))
+    achieved = ev_bytes / (float(dec_ms.sum()) * 1e-3) / 1e9
+    ceiling = probe_ceiling(args, cfg, batches, kv_log_r)
+    # With shared blocks the probe reads every reader's logical bytes while the decode reads
+    # the shared ones once, so the two rates do not compare.
+    shared = any(a != l for a, l in zip(kv_alg_r, kv_log_r))
+    ceiling["frac_of_ceiling"] = None if shared else round(achieved / ceiling["GBps"], 4)
 
     result = {
         "metric": "paged decode attention: achieved KV-read HBM GB/s (% of peak) and seqs/s",
-        "value": round(kv_alg / (ms_per_step * 1e-3) / 1e9, 1),
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -185,7 +194,8 @@ def main() -> int:
             "head_dim": cfg.head_dim, "block_size": cfg.block_size, "max_context_len": cfg.max_context_len,
             "partition_tokens": pkv.partition_tokens(cfg.num_seqs, cfg.num_kv_heads, cfg.max_context_len,
                                                      cfg.partition_size),
-            "kv_bytes_algorithmic": kv_alg, "kv_bytes_logical": kv_logical, "copy_pairs": n_pairs,
+            "kv_bytes_algorithmic_per_replica": kv_alg_r, "kv_bytes_logical_per_replica": kv_log_r,
+            "copy_pairs": n_pairs,
             "replicas": args.replicas, "parallelism": "single GPU",
             "step": "copy_blocks + reshape_and_cache + paged_attention_decode" if args.separate else
                     "copy_blocks + decode_step (cache write fused into the decode launch)",
@@ -197,13 +207,45 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(cfg.name),
                      "kernel": "paged_decode_mfma" if cfg.group_size > 1 else "paged_decode_valu",
-                     "kernel_source_hash": kernel_source_hash()},
+                     "kernel_source_hash": kernel_source_hash(), "ceiling": ceiling},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, batches[0], args.cpu_sample_seqs)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def probe_ceiling(args, cfg, batches, kv_log_r) -> dict:
+    """Rate of the decode read pattern alone on this device: pkv_gather_probe reads the bytes a
+    decode step over each replica reads (the same tiles through the same block tables, with
+    the decode kernels' loads) and does no arithmetic. Timed like the decode launches."""
+    import torch
+
+    import paged_kv_cache_409_amd as pkv
+
+    sinks = [torch.zeros((cfg.num_seqs, cfg.num_kv_heads), dtype=torch.int32, device=b.k_cache.device)
+             for b in batches]
+
+    def run(i):
+        b = batches[i % len(batches)]
+        pkv.gather_probe(b.k_cache, b.v_cache, b.block_tables, b.context_lens, cfg.max_context_len,
+                         sinks[i % len(batches)])
+
+    for i in range(min(args.warmup, 4)):
+        run(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        run(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    read = sum(kv_log_r[i % len(batches)] for i in range(args.steps))
+    return {"kernel": "gather_probe", "GBps": round(read / (float(ms.sum()) * 1e-3) / 1e9, 1),
+            "what": "the K/V tiles of every context read through the block tables with the decode kernels' "
+                    "loads and no arithmetic (logical bytes; pkv_gather_probe)",
+            "us": round(float(ms.mean()) * 1e3, 2)}
 
 
 def prefill_flops(cfg, lay) -> float:

@@ -10,11 +10,12 @@
  *   pkv_decode_step             cache write + attention of one decode step, one launch
  *   pkv_paged_attention_prefill causal attention of prefill chunks over the paged cache
  *   pkv_swap_blocks             move whole blocks between a GPU pool and a pinned host pool
+ *   pkv_gather_probe            measurement aid: the decode read pattern with no arithmetic
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Pointers named *_cache, q, out, key, value, block_tables, context_lens,
- *   query_start_loc, slot_mapping, src_dst_pairs and workspace are DEVICE pointers; every other
+ *   query_start_loc, slot_mapping, src_dst_pairs, workspace and sink are DEVICE pointers; every other
  *   pointer is a host pointer. All tensors are dense, row-major, in the shapes
  *   given below, and 16-byte aligned.
  * - The caller allocates and owns every buffer, including the workspace. The
@@ -280,6 +281,31 @@ int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers
 int pkv_swap_blocks(const void* const* src_k_caches, const void* const* src_v_caches, void* const* dst_k_caches,
                     void* const* dst_v_caches, int num_layers, const int64_t* src_dst_pairs, int num_pairs,
                     int64_t block_bytes, int64_t num_src_blocks, int64_t num_dst_blocks, void* stream);
+
+/*
+ * Measurement aid, not part of the attention path. Decode attention is bound by reading the
+ * cache ("vLLM 推理优化技术深度调研报告", 维度一.3 公式5), and what it can reach is set by
+ * the gather of 16-token tiles through the block tables ("vLLM推理引擎PagedAttention原理与
+ * 性能优化实战", §2.2). This call reads exactly the bytes a decode step over the same batch
+ * reads: for every sequence s and kv head g, the K and V bytes of g in the 16-token tiles
+ * that hold tokens 0 .. context_lens[s] - 1 (whole tiles), found through block_tables as
+ * pkv_paged_attention_decode finds them, with the decode kernels' loads. It computes
+ * nothing but the XOR of every 32-bit word it reads, which it XORs into sink[s *
+ * num_kv_heads + g]; its rate is the ceiling of this access pattern on the device.
+ *
+ *   k_cache, v_cache, block_tables, context_lens, num_seqs, num_kv_heads, head_dim,
+ *   block_size, num_blocks, max_blocks_per_seq, max_context_len, kv_dtype
+ *                  as for pkv_paged_attention_decode (max_context_len: the largest
+ *                  context_lens entry; longer contexts are read only up to it)
+ *   sink           [num_seqs, num_kv_heads] uint32, device, 4-byte aligned; XORed into,
+ *                  so zero it first for the XOR of this call alone
+ *
+ * Block ids outside the pool read as zeros (they contribute nothing to the XOR).
+ */
+int pkv_gather_probe(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                     int64_t num_blocks, int max_blocks_per_seq, int max_context_len, int kv_dtype, uint32_t* sink,
+                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -52,6 +52,11 @@ SIGNATURES = {
         ctypes.POINTER(_c_p), ctypes.POINTER(_c_p),           # src_k_caches src_v_caches
         ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_int,   # dst_k_caches dst_v_caches num_layers
         _c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_p]),         # pairs num_pairs block_bytes num_src num_dst stream
+    "pkv_gather_probe": (_c_int, [
+        _c_p, _c_p, _c_p, _c_p,                        # k_cache v_cache block_tables context_lens
+        _c_int, _c_int, _c_int, _c_int,                # num_seqs num_kv_heads head_dim block_size
+        _c_i64, _c_int, _c_int, _c_int,                # num_blocks max_blocks_per_seq max_context_len kv_dtype
+        _c_p, _c_p]),                                  # sink stream
     "pkv_copy_blocks": (_c_int, [
         ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_int,   # k_caches v_caches num_layers
         _c_p, _c_int, _c_i64, _c_i64, _c_p]),                 # pairs num_pairs block_bytes num_blocks stream

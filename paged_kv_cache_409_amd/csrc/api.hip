@@ -5,6 +5,7 @@
 
 #include "pkv.h"
 #include "pkv_block_manager.h"
+#include "gather_probe.h"
 #include "pkv_launch.h"
 
 
@@ -404,6 +405,41 @@ int pkv_reshape_and_cache(const void* key, const void* value, const int64_t* slo
   const int it = in_dtype == PKV_BF16 ? pkv::kBF16 : pkv::kF16;
   const int kt = kv_dtype == PKV_FP8_E4M3 ? pkv::kFP8 : it;
   return hip_status(pkv::launch_reshape_and_cache(a, it, kt, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int pkv_gather_probe(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                     int64_t num_blocks, int max_blocks_per_seq, int max_context_len, int kv_dtype, uint32_t* sink,
+                     void* stream) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
+    return PKV_ERR_SHAPE;
+  if (!is16bit(kv_dtype) && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  const int shift = block_shift_of(block_size);
+  if (shift < 0 || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+  if ((num_blocks << shift) > 0x7fffffffLL || ((int64_t)max_blocks_per_seq << shift) > 0x7fffffffLL / 16)
+    return PKV_ERR_SHAPE;
+  const long long tiles = ((long long)max_context_len + 15) / 16;
+  const long long chunks = (tiles + pkv::kProbeChunk - 1) / pkv::kProbeChunk;
+  if ((long long)num_seqs * num_kv_heads * chunks > (1LL << 31) - 8) return PKV_ERR_SHAPE;
+  if (num_seqs == 0 || chunks == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_tables || !context_lens || !sink) return PKV_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+    return PKV_ERR_ALIGN;
+  pkv::ProbeArgs a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.sink = sink;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.block_shift = shift;
+  a.num_chunks = (int)chunks;
+  const int tile_bytes = 16 * head_dim * (kv_dtype == PKV_FP8_E4M3 ? 1 : 2);
+  return hip_status(pkv::launch_gather_probe(a, tile_bytes, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers,

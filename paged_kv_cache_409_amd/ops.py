@@ -93,6 +93,26 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
+def gather_probe(k_cache, v_cache, block_tables, context_lens, max_context_len: int, sink: torch.Tensor,
+                 stream=None):
+    """Measurement aid: read the bytes a decode step over this batch reads, XOR them into
+    sink [num_seqs, num_kv_heads] int32 (see pkv_gather_probe)."""
+    _dev(k_cache, v_cache, block_tables, context_lens, sink)
+    NB, Hkv, P, D = k_cache.shape
+    S = context_lens.shape[0]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache / v_cache mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or sink.dtype != torch.int32:
+        raise ValueError("block_tables, context_lens and sink must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(sink.shape) != (S, Hkv):
+        raise ValueError("block_tables / sink shape mismatch")
+    st = _lib.load().pkv_gather_probe(
+        k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, Hkv, D, P, NB,
+        block_tables.shape[1], max_context_len, _dtype(k_cache), sink.data_ptr(), _stream(stream))
+    _check("pkv_gather_probe", st)
+    return sink
+
+
 def decode_step(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens, scale: float,
                 max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
                 workspace: torch.Tensor | None = None, stream=None):

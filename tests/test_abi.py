@@ -163,3 +163,22 @@ def test_swap_argument_errors():
     assert sw(ptrs, ptrs, nullp, ptrs, 1, 16, 2, 4096, 64, 32, None) == -1
     odd = (ctypes.c_void_p * 1)(8)
     assert sw(ptrs, ptrs, odd, ptrs, 1, 16, 2, 4096, 64, 32, None) == -6
+
+
+def test_gather_probe_argument_errors():
+    # Rejected before any launch: fake (aligned) device pointers are never dereferenced.
+    lib = _lib.load()
+    gp = lib.pkv_gather_probe
+    p = 256
+    #          k  v  bt ctx  S  Hkv D   P   NB  maxB maxctx dtype sink stream
+    assert gp(p, p, p, p, 0, 8, 128, 16, 64, 4, 64, 2, p, None) == 0          # no sequences: no-op
+    assert gp(p, p, p, p, 4, 8, 128, 16, 64, 4, 0, 2, p, None) == 0           # no tokens: no-op
+    assert gp(p, p, p, p, 4, 8, 96, 16, 64, 4, 64, 2, p, None) == -4          # head_dim
+    assert gp(p, p, p, p, 4, 8, 128, 24, 64, 4, 64, 2, p, None) == -4         # block size
+    assert gp(p, p, p, p, 4, 8, 128, 16, 64, 4, 64, 9, p, None) == -3         # dtype
+    assert gp(p, p, p, p, 4, 8, 128, 16, 64, 4, 65, 2, p, None) == -2         # context longer than the table row
+    assert gp(p, p, p, p, 4, 0, 128, 16, 64, 4, 64, 2, p, None) == -2         # no kv heads
+    assert gp(p, p, p, p, 4, 8, 128, 16, 64, 4, 64, 2, None, None) == -1      # no sink
+    assert gp(None, p, p, p, 4, 8, 128, 16, 64, 4, 64, 2, p, None) == -1
+    assert gp(p + 8, p, p, p, 4, 8, 128, 16, 64, 4, 64, 2, p, None) == -6     # cache alignment
+    assert gp(p, p, p, p, 4, 8, 128, 16, 64, 4, 64, 2, p + 2, None) == -6     # sink alignment
