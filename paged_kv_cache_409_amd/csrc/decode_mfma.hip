@@ -406,9 +406,19 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
   const int end = min(ctx, start + PB * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
   {
+    // Eight loads in flight per lane (indices past the slice re-read its last entry and are
+    // not stored): a slice of a few hundred blocks costs about one memory latency.
+    constexpr int kBatch = 8;
     const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
-    for (int i = lane; i < nblk; i += kWave)
-      bts[w * PB + i] = tile_name(row, start / kBlock + i, a.block_shift, a.num_blocks);
+    for (int i0 = 0; i0 < nblk; i0 += kBatch * kWave) {
+      int v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        v[k] = tile_name(row, start / kBlock + min(i0 + k * kWave + lane, nblk - 1), a.block_shift, a.num_blocks);
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (i0 + k * kWave + lane < nblk) bts[w * PB + i0 + k * kWave + lane] = v[k];
+    }
   }
   if (lane == 0) {
     ends[w] = end;
@@ -421,8 +431,13 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
   // 2. Wave 0 lists the distinct physical blocks of each logical block, in logical order,
   //    each with the set of sequences that read it.
   if (w == 0) {
+    // The context ends in registers: the list is written to the same LDS allocation, so
+    // reading them there would make every entry written wait for a fresh LDS read.
+    int endr[kMaxSeqsPerGroup];
+#pragma unroll
+    for (int b = 0; b < kMaxSeqsPerGroup; ++b) endr[b] = b < B ? ends[b] : 0;
     int npos = 0;
-    for (int b = 0; b < B; ++b) npos = max(npos, (ends[b] - start + kBlock - 1) / kBlock);
+    for (int b = 0; b < B; ++b) npos = max(npos, (endr[b] - start + kBlock - 1) / kBlock);
     int base = 0;
     for (int i0 = 0; i0 < npos; i0 += kWave) {
       const int i = i0 + lane;
@@ -431,7 +446,7 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
       uint32_t live = 0;
 #pragma unroll
       for (int b = 0; b < kMaxSeqsPerGroup; ++b) {
-        const bool has = b < B && i < npos && pos * kBlock < ends[b];
+        const bool has = b < B && i < npos && pos * kBlock < endr[b];
         ids_b[b] = has ? bts[b * PB + i] : -1;
         live |= has ? (1u << b) : 0u;
       }
@@ -467,8 +482,9 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
       for (int b = 0; b < kMaxSeqsPerGroup; ++b) {
         if (e_readers[b] == 0u) continue;
         int rows = 0;
-        for (int c = 0; c < B; ++c)
-          if ((e_readers[b] >> c) & 1u) rows = max(rows, min(ends[c] - pos * kBlock, kBlock));
+#pragma unroll
+        for (int c = 0; c < kMaxSeqsPerGroup; ++c)
+          if ((e_readers[b] >> c) & 1u) rows = max(rows, min(endr[c] - pos * kBlock, kBlock));
         list_id[e] = e_id[b];
         list_meta[e] = pos | (int)(e_readers[b] << 16) | (rows << 24);
         ++e;
