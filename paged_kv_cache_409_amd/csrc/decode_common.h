@@ -87,6 +87,47 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A work item's block-table slice (the tile names of its partition) is staged in LDS.
+// Its first kBtBatch * kWave entries are loaded at the very start of the item, before
+// the context length is known: their bound comes from the table's row length, so the
+// context length and the slice take one memory latency rather than two in a chain.
+// Entries past the context are loaded but never used.
+constexpr int kBtBatch = 8;
+struct BtSlice {
+  int v[kBtBatch];   // entry k * kWave + lane
+};
+
+__device__ __forceinline__ void prefetch_bt_slice(const DecodeArgs& a, int s, int t0, BtSlice& sl) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
+  // t0 lies inside the table (t0 < max_blocks << shift), so hi >= 1.
+  const int hi = min(a.part_blocks, (a.max_blocks << a.block_shift) - t0);
+#pragma unroll
+  for (int k = 0; k < kBtBatch; ++k)
+    sl.v[k] = tile_name(row, t0 + min(k * kWave + lane, hi - 1), a.block_shift, a.num_blocks);
+}
+
+// Stores entries [0, n) of the slice of sequence s from tile t0 into dst (n <= the
+// prefetch bound): the prefetched ones, then any further ones, eight loads in flight per
+// lane (indices past n re-read entry n - 1 and are not stored).
+__device__ __forceinline__ void store_bt_slice(const DecodeArgs& a, int s, int t0, int n, const BtSlice& sl,
+                                               int* dst) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int k = 0; k < kBtBatch; ++k)
+    if (k * kWave + lane < n) dst[k * kWave + lane] = sl.v[k];
+  const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
+  for (int i0 = kBtBatch * kWave; i0 < n; i0 += kBtBatch * kWave) {
+    int v[kBtBatch];
+#pragma unroll
+    for (int k = 0; k < kBtBatch; ++k)
+      v[k] = tile_name(row, t0 + min(i0 + k * kWave + lane, n - 1), a.block_shift, a.num_blocks);
+#pragma unroll
+    for (int k = 0; k < kBtBatch; ++k)
+      if (i0 + k * kWave + lane < n) dst[i0 + k * kWave + lane] = v[k];
+  }
+}
+
 // Fused step: the work item of partition p of a sequence with (clamped) context length
 // ctx writes that sequence's new token when p holds position ctx - 1 (partition 0 when
 // ctx is 0).

@@ -345,16 +345,14 @@ __device__ __forceinline__ void write_column(const DecodeArgs& a, int s, int hea
 // partition p, which holds tokens [start, ctx) up to the partition's end.
 template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO, bool KLDS>
 __device__ __forceinline__ void mfma_single(const DecodeArgs& a, const int s, const int g, const int p,
-                                            const int ctx, const int start, int* bt_lds, uint8_t* lds,
-                                            uint8_t* tok_rows, const bool writes, const TokenChunk& token) {
+                                            const int ctx, const int start, const BtSlice& sl, int* bt_lds,
+                                            uint8_t* lds, uint8_t* tok_rows, const bool writes,
+                                            const TokenChunk& token) {
   const int lane = threadIdx.x & (kWave - 1), n = lane & 15;
   const int G = a.group;
   const int end = min(ctx, start + a.part_blocks * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
-  {
-    const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
-    for (int i = lane; i < nblk; i += kWave) bt_lds[i] = tile_name(row, start / kBlock + i, a.block_shift, a.num_blocks);
-  }
+  store_bt_slice(a, s, start / kBlock, nblk, sl, bt_lds);
   if (writes) stage_new_token<KVT, D>(token, tok_rows);
   u32x4 qb[D / 32];
   load_q<QT, KVT, D>(a, n < G, s, g * G + n, qb);
@@ -377,60 +375,59 @@ __device__ __forceinline__ void mfma_single(const DecodeArgs& a, const int s, co
 }
 
 // Group mode: the B wavefronts of the workgroup compute sequences s0 .. s0+B-1 of kv head
-// g over partition p together. Every one of them has tokens in the partition.
+// g over partition p together. Every one of them has tokens in the partition. Wave w's
+// sequence s0 + w has context length ctx; its block-table slice was prefetched into sl,
+// and its new token (fused step) is in `token` when token_loaded.
 template <int QT, int KVT, int D>
 __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, const int g, const int p,
-                                           const int start, uint8_t* smem) {
+                                           const int start, const int ctx, const BtSlice& sl,
+                                           TokenChunk token, const bool token_loaded, uint8_t* smem) {
   using Tr = MfmaTraits<QT, KVT, D>;
   const int B = a.seqs_per_group, G = a.group, PB = a.part_blocks;
+  const int lstride = group_list_stride(PB);
   const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1), n = lane & 15, j4 = lane >> 4;
   uint8_t* tiles = smem;
   uint8_t* tok_rows = smem + B * Tr::kLdsBytes;             // B new-token row copies
   int* bts = (int*)(tok_rows + B * kTokenRowsLds);           // B slices of PB block ids
   int* small = bts + B * PB;                                 // kDecodeSmallLds bytes
   int* ends = small;                                         // [kMaxSeqsPerGroup]
-  int* count = small + kMaxSeqsPerGroup;
   float* merge_ml = (float*)(small + 16);                    // [B][16][2]
   int* patch_pos = small + 160;                              // [B] new token's block, -1: none
   int* patch_row = small + 168;                              // [B] its row in the block
-  int* list_id = small + kDecodeSmallLds / 4;                // up to B * PB entries
-  int* list_meta = list_id + B * PB;
+  int* list_id = small + kDecodeSmallLds / 4;                // B lists of up to lstride entries
+  int* list_meta = list_id + B * lstride;
 
   // 1. Each wave stages its sequence's block-table slice and context end, and writes its
-  //    sequence's new token (fused step).
+  //    sequence's new token (fused step). The query fragments are loaded here too, so
+  //    that their latency passes during the listing.
   const int s = s0 + w;
-  const int ctx = min(a.context_lens[s], (a.max_blocks * kBlock) << a.block_shift);
   const bool writes = owns_new_token(a, ctx, p);
-  TokenChunk token = {};
-  if (writes) token = load_new_token<QT, KVT, D>(a, s, g);
+  if (writes && !token_loaded) token = load_new_token<QT, KVT, D>(a, s, g);
   const int end = min(ctx, start + PB * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
-  {
-    // Eight loads in flight per lane (indices past the slice re-read its last entry and are
-    // not stored): a slice of a few hundred blocks costs about one memory latency.
-    constexpr int kBatch = 8;
-    const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
-    for (int i0 = 0; i0 < nblk; i0 += kBatch * kWave) {
-      int v[kBatch];
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k)
-        v[k] = tile_name(row, start / kBlock + min(i0 + k * kWave + lane, nblk - 1), a.block_shift, a.num_blocks);
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k)
-        if (i0 + k * kWave + lane < nblk) bts[w * PB + i0 + k * kWave + lane] = v[k];
-    }
-  }
+  store_bt_slice(a, s, start / kBlock, nblk, sl, bts + w * PB);
   if (lane == 0) {
     ends[w] = end;
     patch_pos[w] = writes && token.written ? (ctx - 1) / kBlock : -1;
     patch_row[w] = (ctx - 1) % kBlock;
   }
   if (writes) stage_new_token<KVT, D>(token, tok_rows + w * kTokenRowsLds);
+  const int ncols = B * G;
+  const bool col_ok = n < ncols;
+  const int cb = col_ok ? n / G : 0;                         // reader (sequence) of column n
+  u32x4 qb[D / 32];
+  load_q<QT, KVT, D>(a, col_ok, s0 + cb, g * G + (col_ok ? n % G : 0), qb);
   __syncthreads();
 
-  // 2. Wave 0 lists the distinct physical blocks of each logical block, in logical order,
-  //    each with the set of sequences that read it.
-  if (w == 0) {
+  // 2. Each wave lists its share of the logical blocks, every B-th one from index w: for
+  //    each, the distinct physical blocks of the B sequences, in logical order, each with
+  //    the set of sequences that read it. Interleaving the logical blocks spreads the
+  //    blocks only one sequence reads (diverged tails) evenly over the waves. Each wave
+  //    then reads the tiles of its own list, so no workgroup barrier is needed between.
+  int* my_id = list_id + w * lstride;
+  int* my_meta = list_meta + w * lstride;
+  int ntiles = 0;
+  {
     // The context ends in registers: the list is written to the same LDS allocation, so
     // reading them there would make every entry written wait for a fresh LDS read.
     int endr[kMaxSeqsPerGroup];
@@ -438,9 +435,8 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
     for (int b = 0; b < kMaxSeqsPerGroup; ++b) endr[b] = b < B ? ends[b] : 0;
     int npos = 0;
     for (int b = 0; b < B; ++b) npos = max(npos, (endr[b] - start + kBlock - 1) / kBlock);
-    int base = 0;
-    for (int i0 = 0; i0 < npos; i0 += kWave) {
-      const int i = i0 + lane;
+    for (int i0 = w; i0 < npos; i0 += B * kWave) {
+      const int i = i0 + lane * B;
       const int pos = start / kBlock + i;
       int ids_b[kMaxSeqsPerGroup];
       uint32_t live = 0;
@@ -477,7 +473,7 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
         total += __popcll(bal);
       }
-      int e = base + before;
+      int e = ntiles + before;
 #pragma unroll
       for (int b = 0; b < kMaxSeqsPerGroup; ++b) {
         if (e_readers[b] == 0u) continue;
@@ -485,30 +481,22 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
 #pragma unroll
         for (int c = 0; c < kMaxSeqsPerGroup; ++c)
           if ((e_readers[b] >> c) & 1u) rows = max(rows, min(endr[c] - pos * kBlock, kBlock));
-        list_id[e] = e_id[b];
-        list_meta[e] = pos | (int)(e_readers[b] << 16) | (rows << 24);
+        my_id[e] = e_id[b];
+        my_meta[e] = pos | (int)(e_readers[b] << 16) | (rows << 24);
         ++e;
       }
-      base += total;
+      ntiles += total;
     }
-    if (lane == 0) *count = base;
   }
-  __syncthreads();
+  wave_lds_sync();
 
-  // 3. Every wave takes entries w, w + B, ... for all of the group's columns.
-  const int ncols = B * G;
-  const bool col_ok = n < ncols;
-  const int cb = col_ok ? n / G : 0;                         // reader (sequence) of column n
-  u32x4 qb[D / 32];
-  load_q<QT, KVT, D>(a, col_ok, s0 + cb, g * G + (col_ok ? n % G : 0), qb);
-  const int total = *count;
-  const int ntiles = total > w ? (total - w + B - 1) / B : 0;
+  // 3. The wave's tiles, for all of the group's columns.
   State<D> st;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
-  mfma_tiles<QT, KVT, D, 2, kPolicyStream, true, true, true>(a, g, ntiles, list_id + w, list_meta + w, B, 0, 0, qb,
+  mfma_tiles<QT, KVT, D, 2, kPolicyStream, true, true, true>(a, g, ntiles, my_id, my_meta, 1, 0, 0, qb,
                                                              col_ok ? (1u << cb) : 0u, col_ok ? ends[cb] : 0,
                                                              tiles + w * Tr::kLdsBytes, st, -1, 0,
                                                              patch_pos, patch_row, tok_rows);
@@ -555,8 +543,10 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
 
   // The values the first decisions need are independent loads, issued together (one
   // memory latency rather than a chain): this wave's context length and the block ids at
-  // logical block i0 of its sequence and of the sequences on either side, and for the
-  // group check the same of every sequence of the group (indices clamped into the batch).
+  // logical block i0 of its sequence and of the sequences on either side, for the group
+  // check the same of every sequence of the group (indices clamped into the batch), then
+  // the wave's block-table slice and, with one partition (where every item writes its
+  // sequence's new token in a fused step), the new token.
   const int i0 = (start / kBlock) >> a.block_shift;   // block of the partition's first tile
   const int max_tokens = (a.max_blocks * kBlock) << a.block_shift;
   const int64_t mb = a.max_blocks;
@@ -566,25 +556,33 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
   const int mine = a.block_tables[s_own * mb + i0];
   const int prev = a.block_tables[max(s_own - 1, 0) * mb + i0];
   const int next = a.block_tables[min(s_own + 1, a.num_seqs - 1) * mb + i0];
+  int grp_ctx[kMaxSeqsPerGroup], grp_first[kMaxSeqsPerGroup];
+#pragma unroll
+  for (int b = 0; b < kMaxSeqsPerGroup; ++b) {
+    const int sb = min(it.s + b, a.num_seqs - 1);
+    grp_ctx[b] = a.context_lens[sb];
+    grp_first[b] = a.block_tables[sb * mb + i0];
+  }
+  BtSlice sl;
+  prefetch_bt_slice(a, s_own, start / kBlock, sl);
+  const bool token_early = a.new_key != nullptr && a.num_parts == 1;
+  TokenChunk token = {};
+  if (token_early) token = load_new_token<QT, KVT, D>(a, s_own, it.g);
 
   // Group mode when every sequence of the group has tokens in this partition and another
   // sequence reads the first sequence's first block of it. Every wave evaluates the same
   // condition, so the whole workgroup takes the same branch.
   if (a.group_mode_ok && it.s + B <= a.num_seqs) {
-    const int first0 = a.block_tables[it.s * mb + i0];
     bool all_live = true, shares = false;
 #pragma unroll
     for (int b = 0; b < kMaxSeqsPerGroup; ++b) {
-      const int sb = min(it.s + b, a.num_seqs - 1);
-      const int c = a.context_lens[sb];
-      const int f = a.block_tables[sb * mb + i0];
       if (b < B) {
-        all_live = all_live && min(c, max_tokens) > start;
-        if (b > 0) shares = shares || f == first0;
+        all_live = all_live && min(grp_ctx[b], max_tokens) > start;
+        if (b > 0) shares = shares || grp_first[b] == grp_first[0];
       }
     }
     if (all_live && shares) {
-      mfma_group<QT, KVT, D>(a, it.s, it.g, it.p, start, smem);
+      mfma_group<QT, KVT, D>(a, it.s, it.g, it.p, start, ctx, sl, token, token_early, smem);
       return;
     }
   }
@@ -592,8 +590,7 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
   // Independent mode: wave w runs sequence it.s + w with its own LDS areas.
   if (s >= a.num_seqs) return;
   const bool writes = owns_new_token(a, ctx, it.p);
-  TokenChunk token = {};
-  if (writes) token = load_new_token<QT, KVT, D>(a, s, it.g);
+  if (writes && !token_early) token = load_new_token<QT, KVT, D>(a, s, it.g);
   if (ctx <= start) {
     if (writes) store_new_token<KVT>(a, token);
     // Nothing in this partition. A whole sequence with no context writes zeros.
@@ -611,11 +608,11 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
   // Does the previous or next sequence of the batch read this sequence's first block?
   const bool shared = (s > 0 && prev == mine) || (s + 1 < a.num_seqs && next == mine);
   if (shared)
-    mfma_single<QT, KVT, D, 2, kPolicyCached, false, false>(a, s, it.g, it.p, ctx, start, bt_lds, lds, tok_rows, writes, token);
+    mfma_single<QT, KVT, D, 2, kPolicyCached, false, false>(a, s, it.g, it.p, ctx, start, sl, bt_lds, lds, tok_rows, writes, token);
   else if (a.num_parts > 1)
-    mfma_single<QT, KVT, D, 2, kPolicyStream, true, true>(a, s, it.g, it.p, ctx, start, bt_lds, lds, tok_rows, writes, token);
+    mfma_single<QT, KVT, D, 2, kPolicyStream, true, true>(a, s, it.g, it.p, ctx, start, sl, bt_lds, lds, tok_rows, writes, token);
   else
-    mfma_single<QT, KVT, D, 1, kPolicyStream, true, true>(a, s, it.g, it.p, ctx, start, bt_lds, lds, tok_rows, writes, token);
+    mfma_single<QT, KVT, D, 1, kPolicyStream, true, true>(a, s, it.g, it.p, ctx, start, sl, bt_lds, lds, tok_rows, writes, token);
 }
 
 template <int QT, int KVT, int D>

@@ -103,7 +103,7 @@ struct VTile {
 // holds tokens [start, ctx) up to the partition's end.
 template <int QT, int KVT, int D, int NBUF, int POLICY, bool PRIO>
 __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, const int ctx, const int start,
-                                          int* bt_lds, uint8_t* tok_rows, const bool writes,
+                                          const BtSlice& sl, int* bt_lds, uint8_t* tok_rows, const bool writes,
                                           const TokenChunk& token) {
   using Tr = ValuTraits<QT, KVT, D>;
   constexpr int LPR = Tr::kLanesPerRow, RPL = Tr::kRowsPerLoad;
@@ -111,12 +111,6 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, co
   const int head = it.g;   // one query head per kv head
   const int end = min(ctx, start + a.part_blocks * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
-  {
-    const int32_t* row = a.block_tables + (int64_t)it.s * a.max_blocks;
-    for (int i = lane; i < nblk; i += kWave) bt_lds[i] = tile_name(row, start / kBlock + i, a.block_shift, a.num_blocks);
-  }
-  if (writes) stage_new_token<KVT, D>(token, tok_rows);
-
   // q columns [col0, col0 + kCols) as packed 16-bit pairs.
   uint32_t qv[Tr::kWords];
   {
@@ -127,6 +121,8 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, co
       qv[x] = w[0]; qv[x + 1] = w[1]; qv[x + 2] = w[2]; qv[x + 3] = w[3];
     }
   }
+  store_bt_slice(a, it.s, start / kBlock, nblk, sl, bt_lds);
+  if (writes) stage_new_token<KVT, D>(token, tok_rows);
   __syncthreads();
   // Fused step: the tile of the new token (the sequence's last position, ctx - 1) gets the
   // token's row from its LDS copy before use; the cache slot still holds stale bytes.
@@ -267,9 +263,16 @@ __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
   const int first_prev = a.block_tables[(int64_t)s_prev * a.max_blocks + i0];
   const int first = a.block_tables[(int64_t)it.s * a.max_blocks + i0];
   const int first_next = a.block_tables[(int64_t)s_next * a.max_blocks + i0];
-  const bool writes = owns_new_token(a, ctx, it.p);
+  // The block-table slice, and with one partition (where every item writes its
+  // sequence's new token in a fused step) the new token, are loaded before the context
+  // length arrives.
+  BtSlice sl;
+  prefetch_bt_slice(a, it.s, start / kBlock, sl);
+  const bool token_early = a.new_key != nullptr && a.num_parts == 1;
   TokenChunk token = {};
-  if (writes) token = load_new_token<QT, KVT, D>(a, it.s, it.g);
+  if (token_early) token = load_new_token<QT, KVT, D>(a, it.s, it.g);
+  const bool writes = owns_new_token(a, ctx, it.p);
+  if (writes && !token_early) token = load_new_token<QT, KVT, D>(a, it.s, it.g);
   if (ctx <= start) {
     if (writes) store_new_token<KVT>(a, token);
     // Nothing in this partition. A whole sequence with no context writes zeros.
@@ -283,9 +286,9 @@ __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
   }
   const bool shared = (it.s > 0 && first_prev == first) || (it.s + 1 < a.num_seqs && first_next == first);
   if (shared)
-    valu_item<QT, KVT, D, NBUF, kPolicyCached, false>(a, it, ctx, start, bt_lds, tok_rows, writes, token);
+    valu_item<QT, KVT, D, NBUF, kPolicyCached, false>(a, it, ctx, start, sl, bt_lds, tok_rows, writes, token);
   else
-    valu_item<QT, KVT, D, NBUF, kPolicyStream, true>(a, it, ctx, start, bt_lds, tok_rows, writes, token);
+    valu_item<QT, KVT, D, NBUF, kPolicyStream, true>(a, it, ctx, start, sl, bt_lds, tok_rows, writes, token);
 }
 
 template <int QT, int KVT, int D>

@@ -30,22 +30,28 @@ struct CacheWriteArgs {
 // Workgroups of the matrix-core decode kernel hold up to this many sequences (one
 // wavefront each).
 constexpr int kMaxSeqsPerGroup = 4;
-// Small LDS area of a group-mode workgroup: per-sequence ends, the tile-list length and
-// the per-wave (max, sum) of every column for the final merge.
+// Small LDS area of a group-mode workgroup: per-sequence context ends, the new tokens'
+// positions and the per-wave (max, sum) of every column for the final merge.
 constexpr int kDecodeSmallLds = 2048;
-// Largest group-mode tile list (entries) a workgroup stages in LDS.
+// Largest number of group-mode tile-list entries (sequences x partition blocks) a
+// workgroup stages in LDS.
 constexpr int kMaxGroupListEntries = 2048;
 
 // LDS copy of one sequence's new token (K row then V row, storage format) in a fused step.
 constexpr int kTokenRowsLds = 512;
 
+// Entries reserved per wavefront for its group-mode tile list: a wave lists every B-th
+// logical block of the partition, each with up to B distinct physical blocks, so at most
+// B * ceil(part_blocks / B) < part_blocks + kMaxSeqsPerGroup entries.
+__host__ __device__ inline int group_list_stride(int part_blocks) { return part_blocks + kMaxSeqsPerGroup; }
+
 // Dynamic LDS bytes of one matrix-core decode workgroup: per-wave K/V tile staging,
 // per-wave new-token rows, per-wave block-table slices, and in group mode the small area
-// and the tile list.
+// and the per-wave tile lists (ids and packed metadata).
 inline size_t mfma_decode_lds_bytes(int head_dim, int seqs_per_group, int part_blocks, bool group_mode) {
   const size_t tile = (size_t)2 * 16 * head_dim * 2;
   return seqs_per_group * (tile + kTokenRowsLds) + (size_t)seqs_per_group * part_blocks * 4 +
-         (group_mode ? kDecodeSmallLds + (size_t)2 * seqs_per_group * part_blocks * 4 : 0);
+         (group_mode ? kDecodeSmallLds + (size_t)2 * seqs_per_group * group_list_stride(part_blocks) * 4 : 0);
 }
 
 // One launch of the prefill-chunk kernel. Work item = (kv head, sequence, tile of

@@ -205,3 +205,25 @@ def test_sharing_groups_match_oracle(G, kv_dtype, tail, width, S, D, partition):
     kc, vc = oracle_caches_after_step(h)
     assert max_err(out, oracle_decode(h, kc, vc)) <= tol(cfg)
     assert torch.equal(out.view(torch.int16), again.view(torch.int16))   # deterministic
+
+
+@pytest.mark.parametrize("partition", [0, 1024])
+@pytest.mark.parametrize("G,kv_dtype", [(4, "fp8_e4m3"), (2, "bf16")])
+def test_long_shared_prefix_groups_match_oracle(G, kv_dtype, partition):
+    # A shared prefix of more logical blocks than one pass of a workgroup's wavefronts
+    # lists at once (B wavefronts x 64 lanes), with diverged tails: the listing takes
+    # several passes per wavefront, in one partition or in several.
+    prompt, tail = 4496, 70
+    cfg = WorkloadConfig(name=f"long_prefix_G{G}_{kv_dtype}", num_seqs=8, num_q_heads=2 * G, num_kv_heads=2,
+                         head_dim=128, num_blocks=4096, seed=57 + G, dtype="bf16", kv_dtype=kv_dtype,
+                         ctx=("beam", prompt, 0, tail, 4), max_context_len=prompt + tail + 1,
+                         kv_scale=(1 / 128 if kv_dtype == "fp8_e4m3" else 1.0))
+    b = device_batch(cfg)
+    h = HostBatch(b)
+    say(cfg.name, "partition", partition)
+    out = gpu_step(b, partition)
+    again = gpu_decode(b, partition_size=partition)
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches_after_step(h)
+    assert max_err(out, oracle_decode(h, kc, vc)) <= tol(cfg)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))   # deterministic
