@@ -30,6 +30,7 @@
  *   such value: an out-of-range block id is read as zeros, an out-of-range slot or
  *   copy pair is skipped, a context length is clamped to the block-table row.
  *   The results of a sequence that hits one of these cases are unspecified.
+ *   pkv_validate_inputs (pkv_validate.h) checks these values, for debugging.
  * - Calls are reentrant; the library holds no global state.
  *
  * Cache layout (chosen for gfx950): k_cache and v_cache are separate tensors of

@@ -15,7 +15,16 @@ PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 1, 2, 3
 
 _c_int, _c_i64, _c_f, _c_p, _c_sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
-# name -> (restype, argtypes), exactly as declared in include/pkv.h and include/pkv_block_manager.h
+
+
+class Validation(ctypes.Structure):
+    """pkv_validation of include/pkv_validate.h."""
+    _fields_ = [("check", ctypes.c_int32), ("reserved", ctypes.c_int32), ("index", ctypes.c_int64),
+                ("value", ctypes.c_int64)]
+
+
+# name -> (restype, argtypes), exactly as declared in include/pkv.h, include/pkv_block_manager.h
+# and include/pkv_validate.h
 SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_c_int]),
     "pkv_api_version": (_c_int, []),
@@ -60,6 +69,15 @@ SIGNATURES = {
     "pkv_copy_blocks": (_c_int, [
         ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_int,   # k_caches v_caches num_layers
         _c_p, _c_int, _c_i64, _c_i64, _c_p]),                 # pairs num_pairs block_bytes num_blocks stream
+    # include/pkv_validate.h (debug checks of index-buffer values)
+    "pkv_validate_inputs_host": (_c_int, [
+        _c_p, _c_p, _c_int, _c_int, _c_int, _c_i64,    # block_tables context_lens num_seqs max_blocks block_size num_blocks
+        _c_p, _c_int, _c_int,                          # slot_mapping num_tokens decode_step
+        _c_p, _c_int, ctypes.POINTER(Validation)]),    # src_dst_pairs num_pairs result
+    "pkv_validate_inputs": (_c_int, [
+        _c_p, _c_p, _c_int, _c_int, _c_int, _c_i64,
+        _c_p, _c_int, _c_int,
+        _c_p, _c_int, _c_p, ctypes.POINTER(Validation)]),   # ... stream result
     # include/pkv_block_manager.h (host-side bookkeeping)
     "pkv_bm_create": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_p)]),
     "pkv_bm_destroy": (None, [_c_p]),

@@ -5,6 +5,7 @@
 
 #include "pkv.h"
 #include "pkv_block_manager.h"
+#include "pkv_validate.h"
 #include "gather_probe.h"
 #include "pkv_launch.h"
 
@@ -491,6 +492,47 @@ int pkv_swap_blocks(const void* const* src_k_caches, const void* const* src_v_ca
   return hip_status(pkv::launch_move_blocks(const_cast<const void* const*>(sk.data()), const_cast<const void* const*>(sv.data()), dk.data(), dv.data(), num_layers,
                                             static_cast<const int64_t*>(pairs), num_pairs, block_bytes,
                                             num_src_blocks, num_dst_blocks, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int pkv_validate_inputs(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                        int max_blocks_per_seq, int block_size, int64_t num_blocks,
+                        const int64_t* slot_mapping, int num_tokens, int decode_step,
+                        const int64_t* src_dst_pairs, int num_pairs, void* stream, pkv_validation* result) {
+  if (!result) return PKV_ERR_NULL;
+  if (num_seqs < 0 || num_tokens < 0 || num_pairs < 0 || max_blocks_per_seq < 0) return PKV_ERR_SHAPE;
+  if ((block_tables != nullptr) != (context_lens != nullptr)) return PKV_ERR_NULL;
+  if (num_pairs > 0 && !src_dst_pairs) return PKV_ERR_NULL;
+  // Host copies of the buffers, then the host checks (which repeat the argument checks).
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::vector<int32_t> bt, cl;
+  std::vector<int64_t> sm, pr;
+  hipError_t e = hipSuccess;
+  if (block_tables) {
+    bt.resize((size_t)num_seqs * max_blocks_per_seq);
+    cl.resize((size_t)num_seqs);
+    if (!bt.empty())
+      e = hipMemcpyAsync(bt.data(), block_tables, bt.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && !cl.empty())
+      e = hipMemcpyAsync(cl.data(), context_lens, cl.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  }
+  if (e == hipSuccess && slot_mapping && num_tokens > 0) {
+    sm.resize((size_t)num_tokens);
+    e = hipMemcpyAsync(sm.data(), slot_mapping, sm.size() * sizeof(int64_t), hipMemcpyDeviceToHost, s);
+  }
+  if (e == hipSuccess && num_pairs > 0) {
+    pr.resize((size_t)num_pairs * 2);
+    e = hipMemcpyAsync(pr.data(), src_dst_pairs, pr.size() * sizeof(int64_t), hipMemcpyDeviceToHost, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  // Empty vectors still need non-null pointers where the caller passed a buffer.
+  static const int32_t kNoInt = 0;
+  static const int64_t kNoLong = 0;
+  return pkv_validate_inputs_host(block_tables ? (bt.empty() ? &kNoInt : bt.data()) : nullptr,
+                                  context_lens ? (cl.empty() ? &kNoInt : cl.data()) : nullptr, num_seqs,
+                                  max_blocks_per_seq, block_size, num_blocks,
+                                  slot_mapping ? (sm.empty() ? &kNoLong : sm.data()) : nullptr, num_tokens,
+                                  decode_step, num_pairs > 0 ? pr.data() : nullptr, num_pairs, result);
 }
 
 }  // extern "C"

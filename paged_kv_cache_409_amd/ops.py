@@ -238,3 +238,45 @@ def swap_blocks(src_k_caches, src_v_caches, dst_k_caches, dst_v_caches, src_dst_
                                      n, src_dst_pairs.data_ptr(), src_dst_pairs.shape[0], block_bytes,
                                      src.shape[0], dst.shape[0], _stream(stream))
     _check("pkv_swap_blocks", st)
+
+
+CHECKS = {0: "ok", 1: "context_len", 2: "block_id", 3: "slot_range", 4: "slot_duplicate", 5: "slot_not_last",
+          6: "slot_shared_block", 7: "pair_range", 8: "pair_duplicate_dst", 9: "pair_dst_is_src"}
+
+
+def validate_inputs(num_blocks: int, block_tables=None, context_lens=None, slot_mapping=None, src_dst_pairs=None,
+                    block_size: int = 16, decode_step: bool = False, stream=None) -> tuple[str, int, int]:
+    """Debug check of the values in the index buffers (see include/pkv_validate.h).
+
+    Returns (check, index, value): ("ok", -1, 0), or the name of the first failed check with
+    where it failed and the offending value. Tensors on the GPU go through
+    pkv_validate_inputs (copied to the host on `stream`), CPU tensors through
+    pkv_validate_inputs_host; all given tensors must be on the same side.
+    """
+    given = [t for t in (block_tables, context_lens, slot_mapping, src_dst_pairs) if t is not None]
+    on_gpu = {bool(t.is_cuda) for t in given}
+    if len(on_gpu) > 1:
+        raise ValueError("index tensors must all be on the GPU or all on the CPU")
+    for t, dt, name in ((block_tables, torch.int32, "block_tables"), (context_lens, torch.int32, "context_lens"),
+                        (slot_mapping, torch.int64, "slot_mapping"), (src_dst_pairs, torch.int64, "src_dst_pairs")):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    S = context_lens.shape[0] if context_lens is not None else 0
+    maxb = block_tables.shape[1] if block_tables is not None and block_tables.dim() == 2 else 0
+    T = slot_mapping.shape[0] if slot_mapping is not None else 0
+    n_pairs = src_dst_pairs.shape[0] if src_dst_pairs is not None else 0
+
+    def ptr(t):
+        return t.data_ptr() if t is not None else None
+
+    res = _lib.Validation()
+    lib = _lib.load()
+    common = (ptr(block_tables), ptr(context_lens), S, maxb, block_size, num_blocks, ptr(slot_mapping), T,
+              1 if decode_step else 0, ptr(src_dst_pairs), n_pairs)
+    if on_gpu == {True}:
+        st = lib.pkv_validate_inputs(*common, _stream(stream), ctypes.byref(res))
+        _check("pkv_validate_inputs", st)
+    else:
+        st = lib.pkv_validate_inputs_host(*common, ctypes.byref(res))
+        _check("pkv_validate_inputs_host", st)
+    return CHECKS.get(res.check, str(res.check)), int(res.index), int(res.value)

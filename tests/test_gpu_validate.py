@@ -1,0 +1,36 @@
+"""Debug checks of index-buffer values, device entry point (pkv_validate_inputs): the
+buffers are copied from the GPU and give the same verdicts as the host entry point."""
+import pytest
+import torch
+
+import paged_kv_cache_409_amd as pkv
+from tests._gpu import say
+from workloads import WorkloadConfig, make_batch
+
+pytestmark = pytest.mark.gpu
+
+
+def test_device_buffers_give_the_host_verdicts():
+    cfg = WorkloadConfig(name="validate_beams_gpu", num_seqs=8, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                         num_blocks=256, seed=5, dtype="bf16", kv_dtype="bf16", ctx=("beam", 64, 0, 40, 4),
+                         max_context_len=64 + 40 + 1)
+    b = make_batch(cfg, "cpu")
+    ctx = b.context_lens.clone()
+    ctx[2] = b.block_tables.shape[1] * 16 + 5
+    sm = b.slot_mapping.clone()
+    sm[6] = sm[1]
+    pairs = b.copy_pairs.clone()
+    pairs[1, 1] = pairs[0, 1]
+    cases = [dict(), dict(context_lens=ctx), dict(slot_mapping=sm), dict(src_dst_pairs=pairs),
+             dict(slot_mapping=None, decode_step=False), dict(block_tables=None, context_lens=None, decode_step=False)]
+    for over in cases:
+        args = dict(block_tables=b.block_tables, context_lens=b.context_lens, slot_mapping=b.slot_mapping,
+                    src_dst_pairs=b.copy_pairs, decode_step=True)
+        args.update(over)
+        host = pkv.validate_inputs(cfg.num_blocks, **args)
+        dev = pkv.validate_inputs(cfg.num_blocks, **{k: (v.cuda() if isinstance(v, torch.Tensor) else v)
+                                                     for k, v in args.items()})
+        say("validate", sorted(over), host)
+        assert dev == host
+    assert pkv.validate_inputs(cfg.num_blocks, b.block_tables.cuda(), b.context_lens.cuda(), b.slot_mapping.cuda(),
+                               b.copy_pairs.cuda(), decode_step=True) == ("ok", -1, 0)
