@@ -199,7 +199,7 @@ def main() -> int:
                                                      cfg.partition_size),
             "kv_bytes_algorithmic_per_replica": kv_alg_r, "kv_bytes_logical_per_replica": kv_log_r,
             "copy_pairs": n_pairs,
-            "replicas": args.replicas, "parallelism": "single GPU",
+            "replicas": args.replicas, "seed": cfg.seed, "parallelism": "single GPU",
             "step": "copy_blocks + reshape_and_cache + paged_attention_decode" if args.separate else
                     "copy_blocks + decode_step (cache write fused into the decode launch)",
         },
@@ -331,7 +331,7 @@ def prefill_bench(args, cfg, dev) -> int:
             "head_dim": cfg.head_dim, "block_size": cfg.block_size, "new_tokens": T, "max_query_len": max(max_q),
             "context_lens_replica0": lay.context_lens.tolist(),
             "flops_algorithmic_per_replica": flops_r, "flops_algorithmic_mean": round(step_flops),
-            "replicas": args.replicas, "parallelism": "single GPU",
+            "replicas": args.replicas, "seed": cfg.seed, "parallelism": "single GPU",
             "step": "reshape_and_cache (chunk) + paged_attention_prefill",
         },
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
