@@ -11,11 +11,15 @@ namespace pkv {
 
 // One workgroup of 256 threads per output row (sequence, q head). Thread (pg, cg) owns
 // columns 4cg..4cg+3 of every partition p = pg (mod kSlices); the kSlices partial sums
-// are added in LDS in a fixed order, so the result does not depend on timing.
+// are added in LDS in a fixed order, so the result does not depend on timing. The
+// pieces of a thread's first kBatch partitions are loaded at once, before the maximum
+// is known, so that up to kSlices * kBatch partitions cost one memory latency; more
+// partitions are read in further rounds.
 template <int QT, int D>
 __global__ __launch_bounds__(256) void paged_decode_reduce(ReduceArgs a) {
   constexpr int kGroups = D / 4;              // column groups of 4 floats
   constexpr int kSlices = 256 / kGroups;      // partition slices
+  constexpr int kBatch = 8;                   // partitions per thread held in registers
   __shared__ float wave_max[256 / kWave];
   __shared__ f32x4 part_acc[kSlices][kGroups];
   __shared__ float part_l[kSlices];
@@ -28,9 +32,23 @@ __global__ __launch_bounds__(256) void paged_decode_reduce(ReduceArgs a) {
   const float* ml = a.part_ml + (int64_t)row * a.num_parts * 2;
   const float* po = a.part_o + (int64_t)row * a.num_parts * D + 4 * cg;
 
+  float mr[kBatch], lr[kBatch];
+  f32x4 orr[kBatch];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int p = pg + k * kSlices;
+    const bool live = p < np;
+    const f32x2 v = live ? *(const f32x2*)(ml + 2 * p) : f32x2{-INFINITY, 0.f};
+    mr[k] = v[0];
+    lr[k] = v[1];
+    orr[k] = live ? *(const f32x4*)(po + (int64_t)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
   // M = max over the partitions' running maxima (log2 units).
-  float m = -INFINITY;
-  for (int p = tid; p < np; p += 256) m = fmaxf(m, ml[2 * p]);
+  float m = mr[0];
+#pragma unroll
+  for (int k = 1; k < kBatch; ++k) m = fmaxf(m, mr[k]);
+  for (int p = kSlices * kBatch + tid; p < np; p += 256) m = fmaxf(m, ml[2 * p]);
 #pragma unroll
   for (int x = kWave / 2; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x, kWave));
   if ((tid & (kWave - 1)) == 0) wave_max[tid / kWave] = m;
@@ -38,10 +56,17 @@ __global__ __launch_bounds__(256) void paged_decode_reduce(ReduceArgs a) {
   float M = wave_max[0];
 #pragma unroll
   for (int w = 1; w < 256 / kWave; ++w) M = fmaxf(M, wave_max[w]);
+  if (M == -INFINITY) M = 0.f;   // no partition (empty context): every weight is exp2(-inf) = 0
 
   float L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int p = pg; p < np; p += kSlices) {
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const float w = exp2_fast(mr[k] - M);     // an empty slot: exp2(-inf) = 0
+    L = fmaf(w, lr[k], L);
+    acc += w * orr[k];
+  }
+  for (int p = pg + kSlices * kBatch; p < np; p += kSlices) {
     const float w = exp2_fast(ml[2 * p] - M);
     L = fmaf(w, ml[2 * p + 1], L);
     acc += w * *(const f32x4*)(po + (int64_t)p * D);

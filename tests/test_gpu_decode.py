@@ -227,3 +227,12 @@ def test_long_shared_prefix_groups_match_oracle(G, kv_dtype, partition):
     kc, vc = oracle_caches_after_step(h)
     assert max_err(out, oracle_decode(h, kc, vc)) <= tol(cfg)
     assert torch.equal(out.view(torch.int16), again.view(torch.int16))   # deterministic
+
+
+@pytest.mark.parametrize("partition", [0, 32768])
+def test_very_long_contexts_match_oracle(partition):
+    # Contexts of 200000 and 131073 tokens (12500 and 8193 blocks): the library's own
+    # split (hundreds of partitions) and the longest partition it accepts.
+    ctx = [200000, 131073]
+    cfg = small_cfg(4, 128, "bf16", "bf16", S=2, Hkv=1, ctx=("fixed", ctx), max_ctx=200000, seed=13)
+    _step_case(cfg, partition)
