@@ -172,11 +172,8 @@ def main() -> int:
     first = args.warmup + args.steps
     ev_bytes = sum(kv_alg_r[(first + i) % len(batches)] for i in range(args.steps))
     achieved = ev_bytes / (float(dec_ms.sum()) * 1e-3) / 1e9
-    ceiling = probe_ceiling(args, cfg, batches, kv_log_r)
-    # With shared blocks the probe reads every reader's logical bytes while the decode reads
-    # the shared ones once, so the two rates do not compare.
-    shared = any(a != l for a, l in zip(kv_alg_r, kv_log_r))
-    ceiling["frac_of_ceiling"] = None if shared else round(achieved / ceiling["GBps"], 4)
+    ceiling = probe_ceiling(args, cfg, batches, kv_log_r, kv_alg_r)
+    ceiling["frac_of_ceiling"] = round(achieved / ceiling["GBps"], 4)
 
     result = {
         "metric": "paged decode attention: achieved KV-read HBM GB/s (% of peak) and seqs/s",
@@ -219,21 +216,61 @@ def main() -> int:
     return 0
 
 
-def probe_ceiling(args, cfg, batches, kv_log_r) -> dict:
+def unique_tile_tables(cfg, lay):
+    """Block tables that name each distinct tile of a sharing group once: for every group
+    of neighbouring sequences the matrix-core decode kernel puts in one workgroup, the
+    distinct physical blocks of each logical block, in logical order (the tiles the decode
+    reads once for all of their readers). Returns (block_tables, context_lens) with one
+    row per group and a context of whole 16-token tiles."""
+    P = cfg.block_size
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    B = min(16 // G, 4) if G > 1 else 1
+    rows = []
+    for g0 in range(0, cfg.num_seqs, B):
+        members = range(g0, min(g0 + B, cfg.num_seqs))
+        nblk = [-(-int(lay.context_lens[s]) // P) for s in members]
+        row = []
+        for j in range(max(nblk)):
+            seen = []
+            for s, n in zip(members, nblk):
+                if j < n and int(lay.block_tables[s, j]) not in seen:
+                    seen.append(int(lay.block_tables[s, j]))
+            row += seen
+        rows.append(row)
+    width = max(len(r) for r in rows)
+    bt = np.zeros((len(rows), width), dtype=np.int32)
+    for i, r in enumerate(rows):
+        bt[i, :len(r)] = r
+    ctx = np.array([len(r) * P for r in rows], dtype=np.int32)
+    return bt, ctx
+
+
+def probe_ceiling(args, cfg, batches, kv_log_r, kv_alg_r) -> dict:
     """Rate of the decode read pattern alone on this device: pkv_gather_probe reads the bytes a
     decode step over each replica reads (the same tiles through the same block tables, with
-    the decode kernels' loads) and does no arithmetic. Timed like the decode launches."""
+    the decode kernels' loads) and does no arithmetic. Timed like the decode launches.
+    Where sequences share blocks, the probe reads each group's distinct tiles once (the
+    decode reads shared blocks once per group), and the rate is counted in unique bytes."""
     import torch
 
     import paged_kv_cache_409_amd as pkv
 
-    sinks = [torch.zeros((cfg.num_seqs, cfg.num_kv_heads), dtype=torch.int32, device=b.k_cache.device)
-             for b in batches]
+    shared = any(a != l for a, l in zip(kv_alg_r, kv_log_r))
+    inputs = []
+    for b in batches:
+        if shared:
+            bt, ctx = unique_tile_tables(cfg, b.layout)
+            dev = b.k_cache.device
+            inputs.append((torch.from_numpy(bt).to(dev), torch.from_numpy(ctx).to(dev), int(ctx.max())))
+        else:
+            inputs.append((b.block_tables, b.context_lens, cfg.max_context_len))
+    sinks = [torch.zeros((c.shape[0], cfg.num_kv_heads), dtype=torch.int32, device=b.k_cache.device)
+             for b, (_, c, _) in zip(batches, inputs)]
 
     def run(i):
         b = batches[i % len(batches)]
-        pkv.gather_probe(b.k_cache, b.v_cache, b.block_tables, b.context_lens, cfg.max_context_len,
-                         sinks[i % len(batches)])
+        bt, ctx, mx = inputs[i % len(batches)]
+        pkv.gather_probe(b.k_cache, b.v_cache, bt, ctx, mx, sinks[i % len(batches)])
 
     for i in range(min(args.warmup, 4)):
         run(i)
@@ -244,10 +281,13 @@ def probe_ceiling(args, cfg, batches, kv_log_r) -> dict:
         evs[i][1].record()
     torch.cuda.synchronize()
     ms = np.array([a.elapsed_time(b) for a, b in evs])
-    read = sum(kv_log_r[i % len(batches)] for i in range(args.steps))
-    return {"kernel": "gather_probe", "GBps": round(read / (float(ms.sum()) * 1e-3) / 1e9, 1),
-            "what": "the K/V tiles of every context read through the block tables with the decode kernels' "
-                    "loads and no arithmetic (logical bytes; pkv_gather_probe)",
+    counted = kv_alg_r if shared else kv_log_r
+    read = sum(counted[i % len(batches)] for i in range(args.steps))
+    what = ("the distinct K/V tiles of each group of neighbouring sequences (what the decode reads once for all "
+            "readers) through the decode kernels' loads and no arithmetic (unique bytes; pkv_gather_probe)") if shared \
+        else ("the K/V tiles of every context read through the block tables with the decode kernels' "
+              "loads and no arithmetic (logical bytes; pkv_gather_probe)")
+    return {"kernel": "gather_probe", "GBps": round(read / (float(ms.sum()) * 1e-3) / 1e9, 1), "what": what,
             "us": round(float(ms.mean()) * 1e3, 2)}
 
 

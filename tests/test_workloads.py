@@ -167,3 +167,25 @@ def test_swap_pairs_are_distinct_and_in_range(name):
     assert not set(out_pairs[:, 0]) & set(in_pairs[:, 1])            # into blocks that were free
     assert out_pairs[:, 0].max() < cfg.gpu_blocks and in_pairs[:, 1].max() < cfg.gpu_blocks
     assert out_pairs[:, 1].max() < cfg.host_blocks
+
+
+def test_unique_tile_tables_name_each_shared_tile_once():
+    # The beam workload's read-pattern ceiling reads each group's distinct tiles once: the
+    # tables it uses name exactly the distinct blocks of every group of 4 neighbouring
+    # beams, in logical order, and cover the unique bytes up to whole tiles.
+    import bench
+    from workloads.gen import kv_bytes_unique, make_layout
+    cfg = CONFIGS["beam_cow"]
+    lay = make_layout(cfg)
+    bt, ctx = bench.unique_tile_tables(cfg, lay)
+    assert bt.shape[0] == cfg.num_seqs // 4 and (ctx % 16 == 0).all()
+    for g in range(bt.shape[0]):
+        names = bt[g, :ctx[g] // 16].tolist()
+        assert len(names) == len(set(names))
+        want = set()
+        for s in range(4 * g, 4 * g + 4):
+            want |= set(lay.block_tables[s, :-(-int(lay.context_lens[s]) // 16)].tolist())
+        assert set(names) == want
+    tile_bytes = 16 * 2 * cfg.num_kv_heads * cfg.head_dim          # fp8: one byte per element
+    unique = kv_bytes_unique(cfg, lay)
+    assert unique <= int(ctx.sum()) // 16 * tile_bytes < unique + bt.shape[0] * 4 * tile_bytes
