@@ -534,7 +534,7 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
   using Tr = MfmaTraits<QT, KVT, D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  const int j = item_of_workgroup(blockIdx.x);
+  const int j = item_of_workgroup(blockIdx.x, a);
   if (j >= a.num_items) return;
   const Item it = decode_item(j, a);
   const int B = a.seqs_per_group;
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(kWave * kMaxSeqsPerGroup, 2) void paged_decode_mfma
 
 template <int QT, int KVT, int D>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const int grid = (a.num_items + 31) / 32 * 32;
+  const int grid = decode_grid(a);
   const size_t lds = mfma_decode_lds_bytes(D, a.seqs_per_group, a.part_blocks, a.group_mode_ok != 0);
   hipLaunchKernelGGL((paged_decode_mfma<QT, KVT, D>), dim3(grid), dim3(kWave * a.seqs_per_group), lds, stream, a);
   return hipGetLastError();

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
   using Tr = ValuTraits<QT, KVT, D>;
   extern __shared__ int bt_lds[];
   __shared__ __attribute__((aligned(16))) uint8_t tok_rows[kTokenRowsLds];
-  const int j = item_of_workgroup(blockIdx.x);
+  const int j = item_of_workgroup(blockIdx.x, a);
   if (j >= a.num_items) return;
   const Item it = decode_item(j, a);
   const int start = it.p * a.part_blocks * kBlock;
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
 
 template <int QT, int KVT, int D>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const int grid = (a.num_items + 31) / 32 * 32;
+  const int grid = decode_grid(a);
   const size_t lds = (size_t)a.part_blocks * sizeof(int);
   hipLaunchKernelGGL((paged_decode_valu<QT, KVT, D, kValuTilesInFlight>), dim3(grid), dim3(kWave), lds, stream, a);
   return hipGetLastError();

@@ -23,11 +23,12 @@ __global__ __launch_bounds__(kWave * kProbeWaves) void gather_probe_kernel(const
   static_assert(L >= 1 && TB % (16 * kWave) == 0, "whole rows per load instruction");
   static_assert(kProbeChunk <= kWave, "one tile name per lane");
   const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const long long item = (long long)blockIdx.x * kProbeWaves + w;   // (kv head, chunk, sequence)
+  // Items (chunk, sequence, kv head), the kv head fastest, as the decode kernels order theirs.
+  const long long item = (long long)blockIdx.x * kProbeWaves + w;
   if (item >= (long long)a.num_seqs * a.num_kv_heads * a.num_chunks) return;   // no barrier below
-  const int s = (int)(item % a.num_seqs);
-  const long long rest = item / a.num_seqs;
-  const int c = (int)(rest % a.num_chunks), g = (int)(rest / a.num_chunks);
+  const int g = (int)(item % a.num_kv_heads);
+  const long long rest = item / a.num_kv_heads;
+  const int s = (int)(rest % a.num_seqs), c = (int)(rest / a.num_seqs);
   const int shift = a.block_shift;
   const int ctx = min(max(a.context_lens[s], 0), (a.max_blocks * kBlock) << shift);
   const int t0 = c * kProbeChunk;
