@@ -490,13 +490,15 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
   }
   wave_lds_sync();
 
-  // 3. The wave's tiles, for all of the group's columns.
+  // 3. The wave's tiles, for all of the group's columns (two tiles in flight, default issue
+  //    priority: with every wave listing its own share, the stepped priority of private
+  //    streams measured 0.7% slower here).
   State<D> st;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
-  mfma_tiles<QT, KVT, D, 2, kPolicyStream, true, true, true>(a, g, ntiles, my_id, my_meta, 1, 0, 0, qb,
+  mfma_tiles<QT, KVT, D, 2, kPolicyStream, false, true, true>(a, g, ntiles, my_id, my_meta, 1, 0, 0, qb,
                                                              col_ok ? (1u << cb) : 0u, col_ok ? ends[cb] : 0,
                                                              tiles + w * Tr::kLdsBytes, st, -1, 0,
                                                              patch_pos, patch_row, tok_rows);
