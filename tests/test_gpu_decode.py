@@ -236,3 +236,12 @@ def test_very_long_contexts_match_oracle(partition):
     ctx = [200000, 131073]
     cfg = small_cfg(4, 128, "bf16", "bf16", S=2, Hkv=1, ctx=("fixed", ctx), max_ctx=200000, seed=13)
     _step_case(cfg, partition)
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 40), (2, 24), (8, 12)])
+def test_kv_head_counts_off_the_xcd_count_match_oracle(G, Hkv):
+    # Work items run in runs of kv heads per XCD; head counts that are not multiples of 8
+    # leave padded, partly empty runs at the end of the grid.
+    cfg = small_cfg(G, 64, "bf16", "bf16", S=5, Hkv=Hkv, ctx=("uniform", 1, 150), max_ctx=150, seed=21)
+    _step_case(cfg)
+    _step_case(cfg, partition_size=64)
