@@ -318,10 +318,12 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, bool valid, int s, i
 }
 
 // Column n's result: out[s, head] (one partition) or the fp32 partial of partition p.
-// `l` is the column's full sum; o holds this lane's rows.
+// `l` is the column's full sum; o holds this lane's rows. The caller writes the 16-row
+// chunks c of D with c mod nw == w (all of them with the defaults); chunk owner 0 also
+// writes the partition's (max, sum).
 template <int QT, int D>
 __device__ __forceinline__ void write_column(const DecodeArgs& a, int s, int head, int p, const f32x4* o,
-                                             float m, float l) {
+                                             float m, float l, int w = 0, int nw = 1) {
   const int j4 = (threadIdx.x & (kWave - 1)) >> 4;
   const int64_t row = (int64_t)s * a.num_q_heads + head;
   if (a.num_parts == 1) {
@@ -329,6 +331,7 @@ __device__ __forceinline__ void write_column(const DecodeArgs& a, int s, int hea
     uint16_t* orow = (uint16_t*)a.out + row * D;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
+      if (c % nw != w) continue;
       const f32x4 v = o[c] * inv;
       *(u32x2*)(orow + 16 * c + 4 * j4) = u32x2{pack2<QT>(v[0], v[1]), pack2<QT>(v[2], v[3])};
     }
@@ -336,8 +339,9 @@ __device__ __forceinline__ void write_column(const DecodeArgs& a, int s, int hea
     const int64_t prow = row * a.num_parts + p;
     float* po = a.part_o + prow * D;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) *(f32x4*)(po + 16 * c + 4 * j4) = o[c];
-    if (j4 == 0) *(f32x2*)(a.part_ml + prow * 2) = f32x2{m, l};
+    for (int c = 0; c < D / 16; ++c)
+      if (c % nw == w) *(f32x4*)(po + 16 * c + 4 * j4) = o[c];
+    if (j4 == 0 && w == 0) *(f32x2*)(a.part_ml + prow * 2) = f32x2{m, l};
   }
 }
 
@@ -505,17 +509,19 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
   if (writes) store_new_token<KVT>(a, token);
   const float l_w = sum_xor32(sum_xor16(st.l));
 
-  // 4. Merge the waves' states column by column (the tile staging area is free again).
+  // 4. Merge the waves' states column by column (the tile staging area is free again). The
+  //    waves share the work: wave w merges and writes the 16-row chunks c of D with
+  //    c mod B == w, for every column.
   __syncthreads();
-  f32x4* merge_o = (f32x4*)tiles;                            // [B][64 lanes][kPv]
+  f32x4* merge_o = (f32x4*)tiles;                            // [B][kPv][64 lanes]
 #pragma unroll
-  for (int c = 0; c < Tr::kPv; ++c) merge_o[(w * kWave + lane) * Tr::kPv + c] = st.o[c];
+  for (int c = 0; c < Tr::kPv; ++c) merge_o[(w * Tr::kPv + c) * kWave + lane] = st.o[c];
   if (j4 == 0) {
     merge_ml[(w * 16 + n) * 2] = st.m;
     merge_ml[(w * 16 + n) * 2 + 1] = l_w;
   }
   __syncthreads();
-  if (w != 0 || !col_ok) return;
+  if (!col_ok) return;
   float M = -INFINITY;
   for (int v = 0; v < B; ++v) M = fmaxf(M, merge_ml[(v * 16 + n) * 2]);
   float L = 0.f;
@@ -526,9 +532,10 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
     const float f = exp2_fast(merge_ml[(v * 16 + n) * 2] - M);   // a wave that saw no token: f = 0
     L = fmaf(f, merge_ml[(v * 16 + n) * 2 + 1], L);
 #pragma unroll
-    for (int c = 0; c < Tr::kPv; ++c) o[c] += f * merge_o[(v * kWave + lane) * Tr::kPv + c];
+    for (int c = 0; c < Tr::kPv; ++c)
+      if (c % B == w) o[c] += f * merge_o[(v * Tr::kPv + c) * kWave + lane];
   }
-  write_column<QT, D>(a, s0 + cb, g * G + n % G, p, o, M, L);
+  write_column<QT, D>(a, s0 + cb, g * G + n % G, p, o, M, L, w, B);
 }
 
 template <int QT, int KVT, int D>
