@@ -233,10 +233,16 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.num_seq_groups = (num_seqs + per_group - 1) / per_group;
   a.group_mode_ok = group_mode ? 1 : 0;
   a.num_items = (int)((long long)a.num_seq_groups * num_kv_heads * plan.num_parts);
-  // Work order (measured; see decode_item): kv head fastest for the vector-ALU kernel and
-  // for matrix-core workgroups of 4 sequences, kv-head-major for smaller workgroups.
-  a.item_order = (group == 1 || per_group >= 4) ? 1 : 0;
-  a.xcd_run = a.item_order == 1 ? num_kv_heads : 4;
+  // Work order (measured; see decode_item): runs of 4 sequences with the kv heads next for
+  // the vector-ALU kernel, kv head fastest for matrix-core workgroups of 4 sequences,
+  // kv-head-major for smaller workgroups.
+  a.item_order = group == 1 ? 2 : (per_group >= 4 ? 1 : 0);
+  a.xcd_run = a.item_order == 2 ? 8 : (a.item_order == 1 ? num_kv_heads : 4);
+  if (a.item_order == 2) {   // whole runs of 4 sequences; the padding items do nothing
+    const long long padded = (long long)(a.num_seq_groups + 3) / 4 * 4 * num_kv_heads * plan.num_parts;
+    if (padded > (1LL << 30)) return PKV_ERR_SHAPE;
+    a.num_items = (int)padded;
+  }
   const float log2e = 1.4426950408889634f;
   const bool fp8 = kv_dtype == PKV_FP8_E4M3;
   a.qk_scale_log2 = scale * log2e * (fp8 ? k_scale : 1.0f);

@@ -254,6 +254,7 @@ __global__ __launch_bounds__(64) void paged_decode_valu(DecodeArgs a) {
   const int j = item_of_workgroup(blockIdx.x, a);
   if (j >= a.num_items) return;
   const Item it = decode_item(j, a);
+  if (it.s >= a.num_seqs) return;   // padding of the last run of 4 sequences
   const int start = it.p * a.part_blocks * kBlock;
   // The context length and the block ids at the partition's first logical block of this
   // sequence and its two neighbours, loaded at once (clamped into the batch).
