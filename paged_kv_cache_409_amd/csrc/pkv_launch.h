@@ -75,7 +75,6 @@ struct PrefillArgs {
   int num_items;                  // num_kv_heads * num_seqs * row_tiles
   float qk_scale_log2;            // scale * log2(e) (* k_scale for an fp8 cache)
   float v_scale;                  // 1, or v_scale for an fp8 cache
-  int cols64;   // EXPERIMENT
 };
 
 // Prefill workgroup: 4 wavefronts x 32 query rows. The fp8-cache kernel takes keys 64
