@@ -189,3 +189,20 @@ def test_unique_tile_tables_name_each_shared_tile_once():
     tile_bytes = 16 * 2 * cfg.num_kv_heads * cfg.head_dim          # fp8: one byte per element
     unique = kv_bytes_unique(cfg, lay)
     assert unique <= int(ctx.sum()) // 16 * tile_bytes < unique + bt.shape[0] * 4 * tile_bytes
+
+
+def test_counter_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    # bench.py reports HBM traffic from a committed counter run only while the kernel
+    # sources hash to the value recorded with it; any other source gives null.
+    import bench
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1")
+    h = bench.kernel_source_hash((str(src),))
+    rec = {"kernel_source_hash": h, "hbm_bytes_per_launch": 1234}
+    (tmp_path / "profiles" / "decode_traffic_w.json").write_text(json.dumps(rec))
+    assert bench.load_traffic("w", sources=(str(src),)) == 1234
+    src.write_text("kernel v2")
+    assert bench.load_traffic("w", sources=(str(src),)) is None
+    assert bench.load_traffic("missing", sources=(str(src),)) is None
