@@ -92,7 +92,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: decode attention shards by kv head or sequence with no exchange, "
-              "and this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+              "so one GPU's rate is the measure; use --gpus 1.", file=sys.stderr)
         return 2
 
     if args.config == "block_manager":
