@@ -1,0 +1,25 @@
+"""The binding has no CPU path: a missing library or host tensors raise errors, never a
+result computed another way."""
+import pytest
+import torch
+
+import paged_kv_cache_409_amd as pkv
+from paged_kv_cache_409_amd import _lib
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libpkv.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        pkv.partition_tokens(8, 8, 4096)
+
+
+def test_host_tensors_are_refused():
+    S, H, D, NB = 2, 8, 128, 4
+    q = torch.zeros(S, H, D, dtype=torch.bfloat16)
+    kc = torch.zeros(NB, 1, 16, D, dtype=torch.bfloat16)
+    bt = torch.zeros(S, 2, dtype=torch.int32)
+    cl = torch.ones(S, dtype=torch.int32)
+    out = torch.empty_like(q)
+    with pytest.raises(ValueError, match="device tensors"):
+        pkv.paged_attention_decode(out, q, kc, kc.clone(), bt, cl, 0.088, 32)
