@@ -4,6 +4,7 @@
     python bench.py --config prefill_70b_gqa      (a prefill-chunk step, see prefill_bench)
     python bench.py --config swap_70b             (blocks out to pinned host memory and back, see swap_bench)
     python bench.py --config block_manager        (host bookkeeping of decode steps, see block_manager_bench)
+    python bench.py --config cache_ops            (reshape_and_cache and copy_blocks per call, see cache_ops_bench)
 
 A step is the whole hot path over one synthetic batch: copy-on-write block copies
 (when the batch has any), the cache write of every sequence's new token, then
@@ -98,10 +99,24 @@ def main() -> int:
     if args.config == "block_manager":
         return block_manager_bench(args)
 
+    from workloads import BLOCK_SIZE_CONFIGS, CONFIGS, PREFILL_CONFIGS, SWAP_CONFIGS
+    # The oracle's worker processes are forked now, before anything touches the GPU.
+    pool = None
+    if not (args.no_cpu_baseline or args.copy_calibration) and args.config not in SWAP_CONFIGS and \
+            args.config != "cache_ops":
+        pool = OraclePool()
+    try:
+        return gpu_bench(args, pool)
+    finally:
+        if pool is not None:
+            pool.close()
+
+
+def gpu_bench(args, pool) -> int:
     import torch
 
     import paged_kv_cache_409_amd as pkv
-    from workloads import CONFIGS, PREFILL_CONFIGS, make_batch
+    from workloads import BLOCK_SIZE_CONFIGS, CONFIGS, PREFILL_CONFIGS, SWAP_CONFIGS, make_batch
     from workloads.gen import kv_bytes_logical, kv_bytes_unique
 
     dev = torch.device("cuda:0")
@@ -109,11 +124,11 @@ def main() -> int:
     if args.copy_calibration:
         return copy_calibration(args, dev)
     if args.config in PREFILL_CONFIGS:
-        return prefill_bench(args, PREFILL_CONFIGS[args.config], dev)
-    from workloads import SWAP_CONFIGS
+        return prefill_bench(args, PREFILL_CONFIGS[args.config], dev, pool)
     if args.config in SWAP_CONFIGS:
         return swap_bench(args, SWAP_CONFIGS[args.config], dev)
-    from workloads import BLOCK_SIZE_CONFIGS
+    if args.config == "cache_ops":
+        return cache_ops_bench(args, dev)
     cfg = {**CONFIGS, **BLOCK_SIZE_CONFIGS}[args.config]
     batches = [make_batch(cfg, dev, replica=r) for r in range(args.replicas)]
     lay = batches[0].layout
@@ -211,7 +226,7 @@ def main() -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, batches[0], args.cpu_sample_seqs)
+        result["cpu_baseline"] = cpu_baseline(pool, cfg, batches[0], args.cpu_sample_seqs)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -301,7 +316,7 @@ def prefill_flops(cfg, lay) -> float:
     return 4.0 * cfg.head_dim * cfg.num_q_heads * keys
 
 
-def prefill_bench(args, cfg, dev) -> int:
+def prefill_bench(args, cfg, dev, pool) -> int:
     """One prefill-chunk step: the cache write of every sequence's chunk of new tokens,
     then causal attention of the chunk over the paged cache. `value` is matrix TFLOP/s of
     the whole step (algorithmic flops / step time); `roofline` reports the attention
@@ -385,43 +400,143 @@ def prefill_bench(args, cfg, dev) -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = prefill_cpu_baseline(cfg, batches[0])
+        result["cpu_baseline"] = prefill_cpu_baseline(pool, cfg, batches[0])
     print(json.dumps(result), flush=True)
     return 0
 
 
-def prefill_cpu_baseline(cfg, b):
-    """Time the float64 prefill oracle, single-threaded, on whole sequences of the batch
-    (as many as fit about CPU_SAMPLE_SECONDS, shortest first)."""
-    import torch
-    from threadpoolctl import threadpool_limits
-
-    from oracle import attention
-
-    def bits(t):
-        t = t.detach().cpu().contiguous()
-        return t.view(torch.int16).numpy().view(np.uint16) if t.element_size() == 2 else t.view(torch.uint8).numpy()
-
-    q, kc, vc = bits(b.q), bits(b.k_cache), bits(b.v_cache)     # the GPU wrote the chunk during timing
-    bt, ctx, qsl = b.block_tables.cpu().numpy(), b.context_lens.cpu().numpy(), b.query_start_loc.cpu().numpy()
+def prefill_cpu_baseline(pool, cfg, b):
+    """Time the float64 prefill oracle over the whole batch, one (sequence, kv head) per task
+    on the worker processes."""
+    ctx, qsl = b.context_lens.cpu().numpy(), b.query_start_loc.cpu().numpy()
     n = np.diff(qsl).astype(np.int64)
     work = n * (ctx - n) + n * (n + 1) // 2
-    order = np.argsort(work)
-    run = lambda seqs: attention.paged_prefill_attention(q, kc, vc, bt, ctx, qsl, cfg.scale, cfg.dtype,
-                                                         cfg.kv_dtype, b.k_scale, b.v_scale, seqs=seqs)
-    with threadpool_limits(limits=1):
-        seqs, dt = [], 0.0
-        while dt < CPU_SAMPLE_SECONDS:        # shortest first, cycling over the batch if it is quick
-            s = int(order[len(seqs) % len(order)])
-            t0 = time.perf_counter()
-            run([s])
-            dt += time.perf_counter() - t0
-            seqs.append(s)
-    flops = 4.0 * cfg.head_dim * cfg.num_q_heads * float(work[seqs].sum())
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
-            "tokens_per_s": round(float(n[seqs].sum()) / dt, 2), "cores": 1, "kind": "oracle",
-            "sample": f"{len(seqs)} sequence runs over the {cfg.num_seqs} sequences (all rows and heads, "
-                      f"shortest first), float64 numpy oracle on one host thread, {dt:.1f} s"}
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    # the GPU wrote the chunk into the pool during timing
+    arrays = dict(q=host_bits(b.q), kc=host_bits(b.k_cache), vc=host_bits(b.v_cache),
+                  bt=b.block_tables.cpu().numpy(), ctx=ctx, qsl=qsl)
+    meta = dict(scale=cfg.scale, dtype=cfg.dtype, kv_dtype=cfg.kv_dtype, k_scale=b.k_scale, v_scale=b.v_scale,
+                group=G)
+    tasks = [(int(s), g) for s in np.argsort(-work) for g in range(cfg.num_kv_heads)]      # longest first
+    dt, passes = pool.timed_passes(arrays, meta, "prefill", tasks)
+    flops = 4.0 * cfg.head_dim * cfg.num_q_heads * float(work.sum())
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "tokens_per_s": round(float(n.sum()) / dt, 2),
+            "cores": pool.workers, "cpus_visible": pool.visible, "cpu_model": pool.model, "kind": "oracle",
+            "sample": f"all {cfg.num_seqs} sequences (all rows and heads), float64 numpy oracle, one (sequence, "
+                      f"kv head) per task on {pool.workers} worker processes; {passes} timed pass(es), "
+                      f"median round {dt:.3f} s per pass"}
+
+
+def cache_ops_bench(args, dev) -> int:
+    """The two cache operations of the step on their own, per call: reshape_and_cache of a
+    70B decode step's 256 new tokens (bf16), of the 70B prefill batch's 4096 chunk tokens,
+    and of the beam step's 256 tokens into an fp8 cache (with the encode); copy_blocks of the
+    beam step's copy-on-write pairs. Each case rotates over --replicas batches. `us` is the
+    time per call of K calls back to back (one event pair around all of them); `us_event` the
+    mean of per-call event pairs, which adds the launch's dispatch latency. Bytes are what the
+    call must move: rows read and slots written (plus the slot list), or source blocks read
+    and destination blocks written."""
+    import torch
+
+    import paged_kv_cache_409_amd as pkv
+    from workloads import CONFIGS, PREFILL_CONFIGS, make_batch
+
+    def timed(call, n_rep):
+        for i in range(args.warmup):
+            call(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            call(i)
+        b.record()
+        torch.cuda.synchronize()
+        per_call = a.elapsed_time(b) / args.steps
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            evs[i][0].record()
+            call(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        ev = np.array([x.elapsed_time(y) for x, y in evs])
+        return per_call, float(ev.mean()), float(np.percentile(ev, 50))
+
+    cases = []
+
+    def add(name, workload, nbytes, call):
+        ms, ev_mean, ev_p50 = timed(call, args.steps)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        cases.append({"op": name, "workload": workload, "bytes_per_call": int(nbytes), "us": round(ms * 1e3, 2),
+                      "us_event": {"mean": round(ev_mean * 1e3, 2), "p50": round(ev_p50 * 1e3, 2)},
+                      "GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
+
+    def write_case(cfg, workload):
+        bs = [make_batch(cfg, dev, replica=r) for r in range(args.replicas)]
+        T, Hkv, D = bs[0].new_k.shape
+        kv_b = 1 if cfg.kv_dtype == "fp8_e4m3" else 2
+        nbytes = T * Hkv * D * (2 * 2 + 2 * kv_b) + T * 8
+
+        def call(i):
+            b = bs[i % len(bs)]
+            pkv.reshape_and_cache(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale, b.v_scale)
+        add("reshape_and_cache", workload, nbytes, call)
+        return bs
+
+    write_case(CONFIGS["llama2_70b_gqa"], "Llama-2-70B GQA decode step: 256 new tokens x 8 kv heads x D 128, bf16")
+    write_case(PREFILL_CONFIGS["prefill_70b_gqa"],
+               "Llama-2-70B GQA prefill chunks: 8 x 512 = 4096 new tokens x 8 kv heads x D 128, bf16")
+    beams = write_case(CONFIGS["beam_cow"], "beam CoW decode step: 256 new tokens x 8 kv heads x D 128, "
+                                            "bf16 in, fp8 E4M3 cache (IEEE division by the scale, RNE)")
+    n_pairs = len(beams[0].copy_pairs)
+    block_bytes = beams[0].k_cache[0].numel() * beams[0].k_cache.element_size()
+
+    def copy_call(i):
+        b = beams[i % len(beams)]
+        pkv.copy_blocks([b.k_cache], [b.v_cache], b.copy_pairs)
+    add("copy_blocks", f"beam CoW decode step: {n_pairs} copy-on-write pairs, one layer, K and V, "
+                       f"{block_bytes} bytes per block per tensor (fp8)", 2 * 2 * n_pairs * block_bytes, copy_call)
+
+    result = {
+        "metric": "cache write and copy-on-write: us per call and GB/s",
+        "value": cases[0]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(cases[0]["us"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 rows; bf16 or fp8 E4M3 caches", "data": "synthetic",
+        "config": {"workload": "reshape_and_cache and copy_blocks at the decode, prefill and beam workloads' sizes "
+                               "(value: the 70B decode step's cache write)",
+                   "replicas": args.replicas, "parallelism": "single GPU"},
+        "cases": cases,
+        "roofline": {"bound": "hbm", "achieved": cases[0]["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": cases[0]["frac_of_hbm_peak"], "traffic": None, "kernel": "reshape_and_cache_kernel",
+                     "note": "launch-bound at these sizes: a few MB per call"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cache_write_cpu_baseline(CONFIGS["beam_cow"], beams[0])
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cache_write_cpu_baseline(cfg, b):
+    """The reshape_and_cache oracle on the beam step's 256 tokens (fp8 encode), one thread.
+    The oracle returns new pools, so each call also copies the two pools."""
+    from oracle import cache_ops
+    _, visible, model = host_cpu()
+    k, v, kc, vc = host_bits(b.new_k), host_bits(b.new_v), host_bits(b.k_cache), host_bits(b.v_cache)
+    sm = b.slot_mapping.cpu().numpy()
+    run = lambda: cache_ops.reshape_and_cache(k, v, sm, kc, vc, cfg.dtype, cfg.kv_dtype, b.k_scale, b.v_scale)
+    run()
+    times = []
+    while len(times) < 3 and sum(times) <= CPU_SAMPLE_SECONDS:
+        t0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    T, Hkv, D = k.shape
+    nbytes = T * Hkv * D * (2 * 2 + 2 * 1) + T * 8
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "us_per_call": round(dt * 1e6, 1), "cores": 1,
+            "cpus_visible": visible, "cpu_model": model, "kind": "oracle",
+            "sample": f"reshape_and_cache of the beam step's {T} tokens into fp8 pools (the oracle copies both "
+                      f"{kc.nbytes} byte pools per call), numpy on one host thread; median of {len(times)} runs"}
 
 
 def swap_bench(args, cfg, dev) -> int:
@@ -517,26 +632,29 @@ def swap_bench(args, cfg, dev) -> int:
 
 
 def swap_cpu_baseline(cfg, gk, gv, hk, hv, out_pairs):
-    """Time the swap oracle (numpy block copies into copies of the destination pools) on host
-    copies of the pools, single-threaded, for about CPU_SAMPLE_SECONDS."""
+    """Time the swap oracle on host copies of the pools. The oracle copies the destination
+    pools and then every pair's blocks in one sequential pass, so it runs on one thread:
+    median of three whole swap-outs after one warm-up (one timed run when a run is longer
+    than CPU_SAMPLE_SECONDS)."""
     import torch
-    from threadpoolctl import threadpool_limits
 
     from oracle import cache_ops
     to_np = lambda ts: [t.detach().cpu().numpy() if t.element_size() == 1 else
                         t.detach().cpu().view(torch.int16).numpy() for t in ts]
     sk, sv, dk, dv = to_np(gk), to_np(gv), to_np(hk), to_np(hv)
-    runs, dt = 0, 0.0
-    with threadpool_limits(limits=1):
-        while dt < CPU_SAMPLE_SECONDS:
-            t0 = time.perf_counter()
-            cache_ops.swap_blocks(sk, sv, dk, dv, out_pairs)
-            dt += time.perf_counter() - t0
-            runs += 1
-    return {"value": round(runs * cfg.bytes_per_direction / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{runs} swap-outs of the whole case ({cfg.bytes_per_direction} bytes each) between host "
-                      f"arrays, numpy oracle on one host thread, {dt:.1f} s"}
+    _, visible, model = host_cpu()
+    cache_ops.swap_blocks(sk, sv, dk, dv, out_pairs)          # warm-up
+    times = []
+    while len(times) < 3 and sum(times) <= CPU_SAMPLE_SECONDS:
+        t0 = time.perf_counter()
+        cache_ops.swap_blocks(sk, sv, dk, dv, out_pairs)
+        times.append(time.perf_counter() - t0)
+    dt, passes = float(np.median(times)), len(times)
+    return {"value": round(cfg.bytes_per_direction / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "cpus_visible": visible, "cpu_model": model, "kind": "oracle",
+            "sample": f"one swap-out of the whole case ({cfg.bytes_per_direction} bytes) between host arrays, "
+                      f"numpy oracle on one host thread (it is one sequential pass); median of {passes} run(s), "
+                      f"{dt:.2f} s each"}
 
 
 def block_manager_bench(args) -> int:
@@ -636,44 +754,129 @@ def copy_calibration(args, dev) -> int:
     return 0
 
 
-def cpu_baseline(cfg, b, sample_seqs: int):
-    """Time the float64 oracle, single-threaded, on a bounded sample of the batch's sequences."""
-    import torch
+def host_cpu():
+    """(workers, CPUs visible to this process, CPU model) for the oracle baselines. The
+    workers are the CPUs this process may run on, capped by OMP_NUM_THREADS where the machine
+    sets it (the host share of one GPU)."""
+    visible = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS") or visible)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return max(1, min(visible, cap)), visible, model
+
+
+_ORACLE_INPUTS = {}
+
+
+def _oracle_worker_init():
     from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)       # one BLAS thread per worker process
+
+
+def _oracle_task(task):
+    """One oracle task in a worker process: the inputs are memory-mapped .npy files in
+    task[0] (loaded once per process), task[1] names the oracle, task[2:] its work item."""
+    import numpy as np
 
     from oracle import attention
+    folder, kind = task[0], task[1]
+    if folder not in _ORACLE_INPUTS:
+        _ORACLE_INPUTS.clear()
+        _ORACLE_INPUTS[folder] = {f[:-4]: np.load(os.path.join(folder, f), mmap_mode="r")
+                                  for f in os.listdir(folder) if f.endswith(".npy")}
+    a = _ORACLE_INPUTS[folder]
+    meta = json.load(open(os.path.join(folder, "meta.json")))
+    if kind == "decode":
+        attention.paged_decode_attention(a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], meta["scale"], meta["dtype"],
+                                         meta["kv_dtype"], meta["k_scale"], meta["v_scale"], seqs=[task[2]])
+    else:                              # one kv head of one prefill sequence
+        s, g, G = task[2], task[3], meta["group"]
+        attention.paged_prefill_attention(a["q"][:, g * G:(g + 1) * G], a["kc"][:, g:g + 1], a["vc"][:, g:g + 1],
+                                          a["bt"], a["ctx"], a["qsl"], meta["scale"], meta["dtype"],
+                                          meta["kv_dtype"], meta["k_scale"], meta["v_scale"], seqs=[s])
+    return 0
 
-    def bits(t):
-        t = t.detach().cpu().contiguous()
-        return t.view(torch.int16).numpy().view(np.uint16) if t.element_size() == 2 else t.view(torch.uint8).numpy()
 
+class OraclePool:
+    """Worker processes for the CPU baseline. They are forked before this process touches
+    the GPU (a process that has initialised the GPU must not be forked or exec'd) and
+    never use it; the inputs reach them as .npy files they memory-map."""
+
+    def __init__(self):
+        import multiprocessing
+        self.workers, self.visible, self.model = host_cpu()
+        self.pool = multiprocessing.get_context("fork").Pool(self.workers, initializer=_oracle_worker_init)
+
+    def timed_passes(self, arrays: dict, meta: dict, kind: str, items):
+        """Wall time of one whole pass over `items`: after a warm-up over the first items, the
+        median of three timed rounds, each as many whole passes as take about a third of
+        CPU_SAMPLE_SECONDS of the workers' time together (so that the sample is about
+        CPU_SAMPLE_SECONDS of CPU work); one single pass when a pass is longer than that.
+        Returns (seconds per pass, passes timed)."""
+        import shutil
+        import tempfile
+        need = sum(int(a.nbytes) for a in arrays.values())
+        # memory-backed files where there is room for them twice over, else the temporary folder
+        shm = "/dev/shm" if os.path.isdir("/dev/shm") and shutil.disk_usage("/dev/shm").free > 2 * need else None
+        folder = tempfile.mkdtemp(prefix="pkv_oracle_", dir=shm)
+        try:
+            for name, arr in arrays.items():
+                np.save(os.path.join(folder, name + ".npy"), np.ascontiguousarray(arr))
+            with open(os.path.join(folder, "meta.json"), "w") as f:
+                json.dump(meta, f)
+            tasks = [(folder, kind, *it) for it in items]
+
+            def one_pass(ts):
+                t0 = time.perf_counter()
+                self.pool.map(_oracle_task, ts, chunksize=1)
+                return time.perf_counter() - t0
+
+            one_pass(tasks[:self.workers] * 2)
+            first = one_pass(tasks)
+            if first * self.workers > CPU_SAMPLE_SECONDS:
+                return first, 1
+            reps = max(1, int(CPU_SAMPLE_SECONDS / 3 / (first * self.workers)))
+            rounds = [one_pass(tasks * reps) / reps for _ in range(3)]
+            return float(np.median(rounds)), 3 * reps
+        finally:
+            shutil.rmtree(folder, ignore_errors=True)
+
+    def close(self):
+        self.pool.terminate()
+        self.pool.join()
+
+
+def host_bits(t):
+    """Raw storage bits of a tensor as a host numpy array (uint16 for 16-bit types)."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.element_size() == 2 else t.view(torch.uint8).numpy()
+
+
+def cpu_baseline(pool, cfg, b, sample_seqs: int):
+    """Time the float64 oracle over the whole batch (or its first `sample_seqs` sequences),
+    one sequence per task on the worker processes."""
     # The pool already holds this step's copies and new tokens (the GPU wrote them during timing).
-    q, kc, vc = bits(b.q), bits(b.k_cache), bits(b.v_cache)
-    bt, ctx = b.block_tables.cpu().numpy(), b.context_lens.cpu().numpy()
-    run = lambda seqs: attention.paged_decode_attention(q, kc, vc, bt, ctx, cfg.scale, cfg.dtype, cfg.kv_dtype,
-                                                        b.k_scale, b.v_scale, seqs=seqs)
-    with threadpool_limits(limits=1):
-        run([0])                                   # warm-up (first-call costs)
-        probe = list(range(min(4, cfg.num_seqs)))
-        t0 = time.perf_counter()
-        run(probe)
-        per_seq = max((time.perf_counter() - t0) / len(probe), 1e-5)
-        want = max(1, int(CPU_SAMPLE_SECONDS / per_seq)) if not sample_seqs else sample_seqs
-        if want <= cfg.num_seqs:
-            passes, seqs = 1, np.linspace(0, cfg.num_seqs - 1, want).round().astype(int).tolist()
-        else:
-            passes, seqs = max(1, round(want / cfg.num_seqs)), list(range(cfg.num_seqs))
-        t0 = time.perf_counter()
-        for _ in range(passes):
-            run(seqs)
-        dt = time.perf_counter() - t0
-    kv = passes * int(ctx[seqs].astype(np.int64).sum()) * 2 * cfg.num_kv_heads * cfg.head_dim * (
+    ctx = b.context_lens.cpu().numpy()
+    arrays = dict(q=host_bits(b.q), kc=host_bits(b.k_cache), vc=host_bits(b.v_cache),
+                  bt=b.block_tables.cpu().numpy(), ctx=ctx)
+    meta = dict(scale=cfg.scale, dtype=cfg.dtype, kv_dtype=cfg.kv_dtype, k_scale=b.k_scale, v_scale=b.v_scale)
+    seqs = list(range(sample_seqs if 0 < sample_seqs < cfg.num_seqs else cfg.num_seqs))
+    dt, passes = pool.timed_passes(arrays, meta, "decode", [(s,) for s in seqs])
+    kv = int(ctx[seqs].astype(np.int64).sum()) * 2 * cfg.num_kv_heads * cfg.head_dim * (
         1 if cfg.kv_dtype == "fp8_e4m3" else 2)
-    what = (f"{len(seqs)} of {cfg.num_seqs} sequences" if passes == 1 else
-            f"{passes} passes over all {cfg.num_seqs} sequences")
-    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "seqs_per_s": round(passes * len(seqs) / dt, 2),
-            "cores": 1, "kind": "oracle",
-            "sample": f"{what} (all heads), float64 numpy oracle on one host thread, {dt:.1f} s"}
+    what = f"all {cfg.num_seqs} sequences" if len(seqs) == cfg.num_seqs else f"{len(seqs)} of {cfg.num_seqs} sequences"
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "seqs_per_s": round(len(seqs) / dt, 2),
+            "cores": pool.workers, "cpus_visible": pool.visible, "cpu_model": pool.model, "kind": "oracle",
+            "sample": f"{what} (all heads, logical KV bytes), float64 numpy oracle, one sequence per task on "
+                      f"{pool.workers} worker processes; {passes} timed pass(es), median round {dt:.3f} s per pass"}
 
 
 if __name__ == "__main__":

@@ -103,7 +103,14 @@ size_t pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int num
                                           int max_context_len, int partition_size);
 
 /*
- * Decode-step attention over a paged KV cache.
+ * Decode-step attention over a paged KV cache. A sequence's K and V live in fixed-size
+ * blocks found through its block table, logical position t in block t / block_size at
+ * offset t % block_size ("vLLM推理引擎PagedAttention原理与性能优化实战", §2.2;
+ * "vLLM 推理优化技术深度调研报告", 维度一.3 公式 3, whose body is lost: this is the plain
+ * O(1) reading). Attention over the gathered K and V is ordinary softmax attention,
+ * equal to attention over the contiguous sequence ("vLLM 推理优化技术深度调研报告",
+ * 维度一.1 误解二 and 维度一.3 公式 4). The pages never mention grouped query heads;
+ * query heads map onto kv heads in consecutive groups.
  *
  * For every sequence s and query head h (kv head g = h / (num_q_heads / num_kv_heads)):
  *   K_s[t] = k_cache[block_tables[s][t / 16], g, t % 16, :]  for t < context_lens[s]

@@ -40,6 +40,19 @@ def _dev(*ts: torch.Tensor) -> None:
             raise ValueError("pkv kernels need contiguous tensors")
 
 
+def _workspace(workspace, need: int, device):
+    """The decode workspace: the caller's (a contiguous uint8 device tensor of at least
+    `need` bytes) or a fresh one; (pointer, bytes), or (None, 0) when none is needed."""
+    if workspace is None:
+        if not need:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _dev(workspace)
+    if workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
+    return workspace.data_ptr(), workspace.numel()
+
+
 def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -79,11 +92,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         raise ValueError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables / context_lens shape mismatch")
-    need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace(workspace, workspace_size(S, Hq, Hkv, D, max_context_len, partition_size),
+                                  q.device)
     st = _lib.load().pkv_paged_attention_decode(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         context_lens.data_ptr(), S, Hq, Hkv, D, P, NB, block_tables.shape[1], max_context_len,
@@ -113,11 +123,7 @@ def gather_probe(k_cache, v_cache, block_tables, context_lens, max_context_len: 
     return sink
 
 
-def decode_step(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens, scale: float,
-                max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
-                workspace: torch.Tensor | None = None, stream=None):
-    """Cache write of every sequence's new token, then decode attention, in one launch
-    (same results as reshape_and_cache followed by paged_attention_decode)."""
+def _step_checks(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens):
     _dev(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens)
     S, Hq, D = q.shape
     NB, Hkv, P, D2 = k_cache.shape
@@ -133,11 +139,18 @@ def decode_step(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables
         raise ValueError("slot_mapping must be int64 [num_seqs]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables / context_lens shape mismatch")
-    need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return S, Hq, Hkv, D, P, NB
+
+
+def decode_step(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens, scale: float,
+                max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+                workspace: torch.Tensor | None = None, stream=None):
+    """Cache write of every sequence's new token, then decode attention, in one launch
+    (same results as reshape_and_cache followed by paged_attention_decode)."""
+    S, Hq, Hkv, D, P, NB = _step_checks(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables,
+                                        context_lens)
+    ws_ptr, ws_bytes = _workspace(workspace, workspace_size(S, Hq, Hkv, D, max_context_len, partition_size),
+                                  q.device)
     st = _lib.load().pkv_decode_step(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), key.data_ptr(), value.data_ptr(),
         slot_mapping.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, Hq, Hkv, D, P, NB,

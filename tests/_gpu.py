@@ -136,7 +136,3 @@ def gpu_prefill_step(b, out=None):
     """A prefill chunk: the cache write of its new tokens, then causal attention over the cache."""
     pkv.reshape_and_cache(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale, b.v_scale)
     return gpu_prefill(b, out)
-
-
-def rows_of(h: HostBatch, seqs):
-    return np.concatenate([np.arange(h.query_start_loc[s], h.query_start_loc[s + 1]) for s in seqs])

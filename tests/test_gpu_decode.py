@@ -42,6 +42,17 @@ def test_decode_step_matches_oracle(G, D, dtype, kv_dtype):
     _step_case(small_cfg(G, D, dtype, kv_dtype))
 
 
+@pytest.mark.parametrize("partition", [0, 48])
+@pytest.mark.parametrize("dtype,kv_dtype", [("bf16", "bf16"), ("f16", "fp8_e4m3")])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [3, 5, 6, 7, 12])
+def test_group_sizes_off_the_powers_of_two_match_oracle(G, D, dtype, kv_dtype, partition):
+    # Query-head groups that do not divide 16: workgroups of 4, 3, 2, 2 and 1 sequences
+    # whose 16 product columns are filled to 12, 15, 12, 14 and 12, and final merges that
+    # split D over 4, 3, 2, 2 and 1 wavefronts.
+    _step_case(small_cfg(G, D, dtype, kv_dtype, S=11), partition)
+
+
 @pytest.mark.parametrize("partition", [16, 48, 256, 512])
 @pytest.mark.parametrize("G,dtype,kv_dtype", [(1, "f16", "f16"), (8, "bf16", "bf16"), (4, "bf16", "fp8_e4m3")])
 def test_split_context_matches_oracle_and_unsplit(G, dtype, kv_dtype, partition):
@@ -184,14 +195,19 @@ def test_fp8_cache_over_every_finite_code():
 @pytest.mark.parametrize("G,kv_dtype,tail,width,S", [(2, "bf16", 40, 4, 16), (4, "bf16", 40, 4, 16),
                                                      (4, "fp8_e4m3", 40, 4, 16), (8, "bf16", 40, 4, 16),
                                                      (4, "bf16", 0, 4, 16), (2, "fp8_e4m3", 17, 4, 16),
-                                                     (4, "bf16", 30, 2, 10), (16, "bf16", 40, 4, 8)])
+                                                     (4, "bf16", 30, 2, 10), (16, "bf16", 40, 4, 8),
+                                                     (3, "bf16", 40, 4, 16), (5, "bf16", 40, 3, 15),
+                                                     (5, "fp8_e4m3", 25, 4, 16), (6, "bf16", 40, 2, 12),
+                                                     (7, "bf16", 20, 4, 16), (12, "fp8_e4m3", 40, 4, 8)])
 def test_sharing_groups_match_oracle(G, kv_dtype, tail, width, S, D, partition):
     # Workgroups of neighbouring sequences that share blocks read each shared block once
     # for all of them; every sharing pattern the beam generator makes (whole prefixes,
     # tails shared by children of one parent, no private tail at all) against the oracle.
     # Width-2 beams in workgroups of 4 put two requests in one workgroup and leave a
     # partial last workgroup (independent mode); 16 heads per kv head leave one sequence
-    # per workgroup (shared blocks then take the cached path).
+    # per workgroup (shared blocks then take the cached path). Groups of 3, 5, 6 and 7
+    # heads give workgroups of 4, 3, 2 and 2 sequences with partly filled columns; beams
+    # of width 3 with 3-sequence workgroups put each request in a workgroup of its own.
     cfg = WorkloadConfig(name=f"groups_G{G}_{kv_dtype}_D{D}_t{tail}_w{width}", num_seqs=S, num_q_heads=2 * G,
                          num_kv_heads=2, head_dim=D, num_blocks=2048, seed=31 + G + tail, dtype="bf16",
                          kv_dtype=kv_dtype, ctx=("beam", 96, 0, tail, width), max_context_len=96 + tail + 1,

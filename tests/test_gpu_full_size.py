@@ -1,7 +1,7 @@
 """The five workloads at their full sizes, in the launch configuration the benchmark
 times: one whole decode step (copy-on-write copies, cache write, attention) on the GPU
-against the oracle. Cache contents are compared bit for bit over the whole pool;
-attention outputs on a sample of sequences (all heads, all columns)."""
+against the oracle. Cache contents are compared bit for bit over the whole pool, and
+the attention output of every sequence, head and column against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -11,13 +11,6 @@ from tests._paged import torch_bits
 from workloads import CONFIGS, make_batch
 
 pytestmark = pytest.mark.gpu
-
-
-def _sample(ctx: np.ndarray, n: int = 12):
-    order = np.argsort(ctx, kind="stable")
-    pick = set(np.linspace(0, len(ctx) - 1, n).round().astype(int).tolist())
-    pick |= {int(order[0]), int(order[-1])}                   # shortest and longest
-    return sorted(pick)
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama2_7b", "llama2_70b_gqa", "long_cot", "beam_cow"])
@@ -32,10 +25,7 @@ def test_full_size_step_matches_oracle(name):
     kc, vc = oracle_caches_after_step(h)
     np.testing.assert_array_equal(torch_bits(b.k_cache), kc)
     np.testing.assert_array_equal(torch_bits(b.v_cache), vc)
-    seqs = _sample(h.context_lens) if cfg.num_seqs > 16 else list(range(cfg.num_seqs))
-    ref = oracle_decode(h, kc, vc, seqs=seqs)
-    err = max_err(out, ref, seqs)
-    say(name, "max abs error", err, "over", len(seqs), "sequences")
+    say(name, "oracle over all", cfg.num_seqs, "sequences")
+    err = max_err(out, oracle_decode(h, kc, vc))
+    say(name, "max abs error", err)
     assert err <= tol(cfg)
-    g = out.float()
-    assert torch.isfinite(g).all()
