@@ -178,6 +178,39 @@ int pkv_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
                     int64_t q_seq_stride, int64_t key_stride, int64_t value_stride, int partition_size,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the device scratch array that pkv_decode_step_no_alloc uses in place of a
+ * workspace: one array per GPU, held from the library's load on that GPU until the process
+ * ends. */
+#define PKV_NO_ALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * pkv_decode_step for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments, checks
+ * and results as pkv_decode_step, without the workspace: the split-context partials
+ * [num_seqs, num_q_heads, num_partitions, head_dim + 2] fp32 go to a scratch array inside
+ * the library (PKV_NO_ALLOC_SCRATCH_BYTES on each GPU). The call allocates and frees
+ * nothing; its first call on a GPU looks up the address of that GPU's array.
+ *
+ * Returns PKV_ERR_WORKSPACE, before any launch, when the partials would need more than
+ * PKV_NO_ALLOC_SCRATCH_BYTES (pkv_paged_attention_workspace_size gives their size; the
+ * library's own choice of partitions, partition_size = 0, needs at most about 17 MiB).
+ * The array keeps whatever the last call left in it; every call writes the partials it
+ * reads, so nothing needs clearing.
+ *
+ * All calls on one GPU share that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or unordered calls from several threads) race and give unspecified
+ * outputs. Calls ordered on one stream are safe. The work runs on the device of `stream`
+ * (the current device for NULL).
+ */
+int pkv_decode_step_no_alloc(void* out, const void* q, void* k_cache, void* v_cache,
+                             const void* key, const void* value, const int64_t* slot_mapping,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                             int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
+                             int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
+                             int64_t q_seq_stride, int64_t key_stride, int64_t value_stride, int partition_size,
+                             void* stream);
+
 /*
  * Attention of prefill chunks over a paged KV cache. Long prompts are cut into chunks
  * that run between decode steps ("vLLM推理引擎PagedAttention原理与性能优化实战", §六);

@@ -12,6 +12,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 1, 2, 3
+PKV_NO_ALLOC_SCRATCH_BYTES = 32 << 20     # include/pkv.h
 
 _c_int, _c_i64, _c_f, _c_p, _c_sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -46,6 +47,15 @@ SIGNATURES = {
         _c_int, _c_int, _c_f, _c_f, _c_f,              # q_dtype kv_dtype scale k_scale v_scale
         _c_i64, _c_i64, _c_i64, _c_int,                # q_seq_stride key_stride value_stride partition_size
         _c_p, _c_sz, _c_p]),                           # workspace workspace_bytes stream
+    "pkv_decode_step_no_alloc": (_c_int, [
+        _c_p, _c_p, _c_p, _c_p,                        # out q k_cache v_cache
+        _c_p, _c_p, _c_p,                              # key value slot_mapping
+        _c_p, _c_p,                                    # block_tables context_lens
+        _c_int, _c_int, _c_int, _c_int, _c_int,        # num_seqs num_q_heads num_kv_heads head_dim block_size
+        _c_i64, _c_int, _c_int,                        # num_blocks max_blocks_per_seq max_context_len
+        _c_int, _c_int, _c_f, _c_f, _c_f,              # q_dtype kv_dtype scale k_scale v_scale
+        _c_i64, _c_i64, _c_i64, _c_int,                # q_seq_stride key_stride value_stride partition_size
+        _c_p]),                                        # stream
     "pkv_paged_attention_prefill": (_c_int, [
         _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,      # out q k_cache v_cache block_tables context_lens qsl
         _c_int, _c_int, _c_int, _c_int, _c_int,        # num_seqs num_tokens num_q_heads num_kv_heads head_dim

@@ -1,6 +1,7 @@
 // C ABI of libpkv.so: host-side validation and dispatch. Contract in include/pkv.h.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "pkv.h"
@@ -307,6 +308,62 @@ int pkv_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, scale,
                      k_scale, v_scale, q_seq_stride, partition_size, &tok, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// Split-context partials of pkv_decode_step_no_alloc: a fixed array in the library's
+// device image, so that the entry point needs no allocation. Host code never passes this
+// name to a kernel (on the host it is only a stand-in for the symbol); it uses the device
+// address looked up per GPU below.
+static __device__ __align__(256) uint8_t scratch[PKV_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices];   // device address of `scratch` on each GPU, once looked up
+
+// Device address of `scratch` on the GPU that runs `stream`. The first call for a GPU looks
+// it up with that GPU current (each GPU holds its own copy of the array at its own address).
+int scratch_address(hipStream_t stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return PKV_ERR_HIP;
+  int dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return PKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return PKV_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return PKV_ERR_HIP;
+    if (e != hipSuccess || !p) return PKV_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_decode_step_no_alloc(void* out, const void* q, void* k_cache, void* v_cache,
+                             const void* key, const void* value, const int64_t* slot_mapping,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                             int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
+                             int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
+                             int64_t q_seq_stride, int64_t key_stride, int64_t value_stride, int partition_size,
+                             void* stream) {
+  void* ws = nullptr;
+  const int st = scratch_address(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (st != PKV_OK) return st;
+  const NewTokens tok{key, value, slot_mapping, key_stride, value_stride};
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, scale,
+                     k_scale, v_scale, q_seq_stride, partition_size, &tok, ws, PKV_NO_ALLOC_SCRATCH_BYTES, stream);
 }
 
 int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

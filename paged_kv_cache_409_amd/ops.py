@@ -160,6 +160,23 @@ def decode_step(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables
     return out
 
 
+def decode_step_no_alloc(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens,
+                         scale: float, max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0,
+                         partition_size: int = 0, stream=None):
+    """decode_step without a workspace and without any allocation, by this binding or the
+    library: split-context partials go to the library's fixed scratch array of the GPU
+    (see pkv_decode_step_no_alloc; calls that overlap in time on one GPU race)."""
+    S, Hq, Hkv, D, P, NB = _step_checks(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables,
+                                        context_lens)
+    st = _lib.load().pkv_decode_step_no_alloc(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), key.data_ptr(), value.data_ptr(),
+        slot_mapping.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, Hq, Hkv, D, P, NB,
+        block_tables.shape[1], max_context_len, _dtype(q), _dtype(k_cache), scale, k_scale, v_scale, 0, 0, 0,
+        partition_size, _stream(stream))
+    _check("pkv_decode_step_no_alloc", st)
+    return out
+
+
 def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float,
                             max_query_len: int, k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
     """Causal attention of each sequence's chunk of new tokens (rows query_start_loc[s] ..
