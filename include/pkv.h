@@ -8,6 +8,7 @@
  *   pkv_reshape_and_cache       write each new token's K/V row into its cache slot
  *   pkv_copy_blocks             copy-on-write copies of whole KV blocks
  *   pkv_decode_step             cache write + attention of one decode step, one launch
+ *   pkv_decode_step_no_alloc    the same step without a workspace, for callers that cannot allocate
  *   pkv_paged_attention_prefill causal attention of prefill chunks over the paged cache
  *   pkv_swap_blocks             move whole blocks between a GPU pool and a pinned host pool
  *   pkv_gather_probe            measurement aid: the decode read pattern with no arithmetic
@@ -19,8 +20,10 @@
  *   pointer is a host pointer. All tensors are dense, row-major, in the shapes
  *   given below, and 16-byte aligned.
  * - The caller allocates and owns every buffer, including the workspace. The
- *   library allocates no device memory and keeps no pointer after a call returns.
- *   Buffers must stay alive until the stream has passed the enqueued work.
+ *   library allocates no device memory and keeps no pointer after a call returns;
+ *   its one device buffer is the fixed scratch array of pkv_decode_step_no_alloc,
+ *   part of its device image. Buffers must stay alive until the stream has passed
+ *   the enqueued work.
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  * - Arguments are checked on the host before anything is enqueued; a violation
  *   returns a negative pkv_status and enqueues nothing. No call aborts or throws.
@@ -31,7 +34,9 @@
  *   copy pair is skipped, a context length is clamped to the block-table row.
  *   The results of a sequence that hits one of these cases are unspecified.
  *   pkv_validate_inputs (pkv_validate.h) checks these values, for debugging.
- * - Calls are reentrant; the library holds no global state.
+ * - Calls are reentrant. The only global state is the per-GPU address of that scratch
+ *   array, looked up once; calls of pkv_decode_step_no_alloc that overlap in time on one
+ *   GPU share the array itself.
  *
  * Cache layout (chosen for gfx950): k_cache and v_cache are separate tensors of
  * shape [num_blocks, num_kv_heads, block_size, head_dim] with block_size 16 (the
