@@ -383,6 +383,8 @@ int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache, c
   if (shift < 0 || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
   if ((num_blocks << shift) > 0x7fffffffLL || ((int64_t)max_blocks_per_seq << shift) > 0x7fffffffLL / 16)
     return PKV_ERR_SHAPE;
+  // tile positions in one kv head's view of the pool are ints
+  if ((num_blocks << shift) * num_kv_heads > 0x7fffffffLL) return PKV_ERR_SHAPE;
   if (!(std::isfinite(scale) && scale > 0.f)) return PKV_ERR_SHAPE;
   const bool fp8 = kv_dtype == PKV_FP8_E4M3;
   if (fp8 && !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))

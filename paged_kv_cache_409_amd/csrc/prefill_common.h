@@ -28,6 +28,15 @@ __device__ __forceinline__ float dot2_ones(uint32_t p, float acc) {
   }
 }
 
+// Position of a named tile in one kv head's view of the pool, in units of one 16-token
+// tile (-1 stays -1): block b's tiles of one kv head lie num_kv_heads << shift tiles apart.
+// The prefill kernels stage positions rather than names, so that a load's address is the
+// staged value times the tile size (a few scalar instructions per load instead of about
+// fifteen); the host keeps (num_blocks << shift) * num_kv_heads within an int.
+__device__ __forceinline__ int tile_position(int v, int shift, int num_kv_heads) {
+  return v < 0 ? -1 : (v >> shift) * (num_kv_heads << shift) + (v & ((1 << shift) - 1));
+}
+
 constexpr float kLazyRescale = 8.0f;
 constexpr int kIdsRing = 1024;   // block-table entries a workgroup keeps in LDS
 

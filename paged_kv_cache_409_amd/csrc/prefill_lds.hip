@@ -135,13 +135,14 @@ __global__ __launch_bounds__(kWave * W, 3) void paged_prefill_lds(const PrefillA
 
   // ---- tile names and direct-to-LDS loads ----------------------------------------------------
   const int64_t head_stride = (int64_t)Tr::kTile16 << shift;
-  const int64_t block_stride = (int64_t)a.num_kv_heads * head_stride;
   const uint8_t* kbase = (const uint8_t*)a.k_cache + (int64_t)g * head_stride;
   const uint8_t* vbase = (const uint8_t*)a.v_cache + (int64_t)g * head_stride;
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
-  auto fill_ids = [&](int first) {   // names of 16-token tiles [first, first + kIdsRing)
-    for (int k = t; k < kIdsRing; k += Tr::kThreads)
-      ids_lds[k] = first + k < ntiles ? tile_name(bt, first + k, shift, a.num_blocks) : -1;
+  auto position = [&](int tt) {   // of 16-token tile tt of the context, or -1
+    return tt < ntiles ? tile_position(tile_name(bt, tt, shift, a.num_blocks), shift, a.num_kv_heads) : -1;
+  };
+  auto fill_ids = [&](int first) {   // positions of 16-token tiles [first, first + kIdsRing)
+    for (int k = t; k < kIdsRing; k += Tr::kThreads) ids_lds[k] = position(first + k);
   };
   auto read_ids = [&](int i) -> u32x2 {   // the two 16-token tiles of stage tile i
     return *(const u32x2*)(ids_lds + ((i * (kLdsKeys / kBlock)) & (kIdsRing - 1)));
@@ -163,9 +164,9 @@ __global__ __launch_bounds__(kWave * W, 3) void paged_prefill_lds(const PrefillA
 #pragma unroll
     for (int u = 0; u < Tr::kLoads; ++u) {
       const int sub = ((u * W + w) * 1024) / Tr::kRow / kBlock;   // 16-token tile of this instruction
-      const int id = readfirstlane((int)(sub == 0 ? ids[0] : ids[1]));
+      const int id = readfirstlane((int)(sub == 0 ? ids[0] : ids[1]));   // tile position
       const bool live = id >= 0;
-      const int64_t off = live ? tile_offset(id, shift, block_stride, Tr::kTile16) : 0;
+      const int64_t off = live ? (int64_t)id * Tr::kTile16 : 0;
       const uint32_t bytes = live ? (uint32_t)Tr::kTile16 : 0u;
       // rows past the workgroup's last key load as zeros (offset past the buffer)
       const bool row_live = i * kLdsKeys + rrow[u] < kv_end;
@@ -291,11 +292,10 @@ __global__ __launch_bounds__(kWave * W, 3) void paged_prefill_lds(const PrefillA
   __syncthreads();
   issue_loads(Stage<0>{}, 0, read_ids(0));
   issue_loads(Stage<1>{}, 1, read_ids(1));
-  // Stage tile 2's names come from the table itself: a read of the ring here would be
+  // Stage tile 2's positions come from the table itself: a read of the ring here would be
   // merged with the one at the end of the loop into a single read through a pointer the
   // compiler can no longer tie to the ring, and it would then wait for every load in flight.
-  u32x2 ids = {(uint32_t)(4 < ntiles ? tile_name(bt, 4, shift, a.num_blocks) : -1),
-               (uint32_t)(5 < ntiles ? tile_name(bt, 5, shift, a.num_blocks) : -1)};
+  u32x2 ids = {(uint32_t)position(4), (uint32_t)position(5)};
   // Stage tile i sits in stage i mod 3; tile i + 2 goes into the stage read at i - 1.
   auto iteration = [&](auto stg, int i) {
     constexpr int S = decltype(stg)::value;

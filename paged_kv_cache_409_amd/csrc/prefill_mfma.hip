@@ -112,18 +112,19 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
 
   // ---- K/V tiles: global -> registers -> LDS ----------------------------------------------
   const int64_t head_stride = (int64_t)Tr::kBlockBytes << shift;   // one kv head's slice of a block
-  const int64_t block_stride = (int64_t)a.num_kv_heads * head_stride;
   const uint8_t* kbase = (const uint8_t*)a.k_cache + (int64_t)g * head_stride;
   const uint8_t* vbase = (const uint8_t*)a.v_cache + (int64_t)g * head_stride;
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
 
-  // The names of the 16-token tiles (block * 2^shift + sub-tile, -1 past the last tile or
-  // for a block id out of the pool) are staged in an LDS ring of kIdsRing entries,
+  // The positions of the 16-token tiles (tile_position of their names; -1 past the last
+  // tile or for a block id out of the pool) are staged in an LDS ring of kIdsRing entries,
   // refilled by the whole workgroup when the walk reaches its end. A key tile's four names
   // are read from the ring one iteration before its loads are issued.
   auto fill_ids = [&](int first) {   // tiles [first, first + kIdsRing); first is a multiple of kIdsRing
     for (int k = t; k < kIdsRing; k += Tr::kThreads)
-      ids_lds[k] = first + k < ntiles ? tile_name(bt, first + k, shift, a.num_blocks) : -1;
+      ids_lds[k] = first + k < ntiles
+                       ? tile_position(tile_name(bt, first + k, shift, a.num_blocks), shift, a.num_kv_heads)
+                       : -1;
   };
   auto read_ids = [&](int i) -> u32x4 {   // ids of tile i's four blocks (same address in every lane)
     return *(const u32x4*)(ids_lds + ((i * (kPrefillKeys / kBlock)) & (kIdsRing - 1)));
@@ -143,8 +144,8 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void paged_prefill_mfma(c
     for (int u = 0; u < Tr::kLoads; ++u) {
       const int j = (u * Tr::kThreads + w * kWave) / Tr::kChunksPerBlock;
       const int id = j == 0 ? id0 : j == 1 ? id1 : j == 2 ? id2 : id3;
-      const bool live = id >= 0;                                    // ids are tile names
-      const int64_t off = live ? tile_offset(id, shift, block_stride, Tr::kBlockBytes) : 0;
+      const bool live = id >= 0;                                    // ids are tile positions
+      const int64_t off = live ? (int64_t)id * Tr::kBlockBytes : 0;
       const uint32_t bytes = live ? (uint32_t)Tr::kBlockBytes : 0u;   // 0: loads return zeros
       const uint32_t c16 = (uint32_t)((u * Tr::kThreads + t) % Tr::kChunksPerBlock) * 16;
       rk[u] = buf_load16<kPolicyCached>(make_rsrc(kbase + off, bytes), c16);

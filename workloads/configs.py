@@ -92,7 +92,13 @@ PREFILL_70B_GQA = WorkloadConfig(
     description="Llama-2-70B GQA layer, chunked prefill: 8 seqs, 512-token chunks after cached "
                 "prefixes of 0-3584 tokens (ctx U[512,4096]), 64 q / 8 kv heads, D 128, bf16")
 
-PREFILL_CONFIGS = {c.name: c for c in (PREFILL_TINY, PREFILL_70B_GQA)}
+# The same batch with an FP8 cache ("vLLM推理引擎PagedAttention原理与性能优化实战", §5.2), served
+# by the kernel that widens fp8 tiles on their way into LDS.
+PREFILL_70B_GQA_FP8 = replace(PREFILL_70B_GQA, name="prefill_70b_gqa_fp8", kv_dtype="fp8_e4m3", kv_scale=1.0 / 128.0,
+                              description="Llama-2-70B GQA layer, chunked prefill as prefill_70b_gqa, with an "
+                                          "fp8-e4m3 cache (per-tensor scale 1/128), bf16 q")
+
+PREFILL_CONFIGS = {c.name: c for c in (PREFILL_TINY, PREFILL_70B_GQA, PREFILL_70B_GQA_FP8)}
 
 # The block-size question of "vLLM 推理优化技术深度调研报告", 维度四.5 (bigger pages: fewer
 # table entries, more internal fragmentation): the Llama-2-70B GQA decode layer with
