@@ -204,7 +204,15 @@ __device__ __forceinline__ void mfma_tiles(const DecodeArgs& a, const int g, con
   uint8_t* kl = lds;
   uint8_t* vl = lds + Tr::kTileLds;
 
-  auto process = [&](Tile<QT, KVT, D>& t) {
+  // Processes tile t. With one tile in flight its registers are reloaded with tile `next`
+  // as soon as they are free (after staging for K through LDS, after the QK products for K
+  // in registers), so that the next tile's loads overlap this tile's products and softmax
+  // (1.3% on the 70B batch). With two tiles in flight the reload follows the processing: a
+  // third tile's worth of loads in flight measured slower there.
+  constexpr bool kEarly = NBUF == 1;
+  auto process = [&](Tile<QT, KVT, D>& t, const int next) {
+    const int pos = t.pos;
+    const uint32_t readers_of = t.readers;
     // Fused step: swap the new token's row into the tile.
     int trow = -1;
     const uint8_t* tsrc = tok_rows;
@@ -231,6 +239,7 @@ __device__ __forceinline__ void mfma_tiles(const DecodeArgs& a, const int g, con
     // V rows past every reader's context are zeroed.
     if constexpr (KLDS) stage(t.k, kl, false, 0);
     stage(t.v, vl, t.rows < kBlock, t.rows);
+    if constexpr (kEarly && KLDS) load(t, next);
     wave_lds_sync();
 
     // S^T = K . Q^T for this block.
@@ -251,9 +260,10 @@ __device__ __forceinline__ void mfma_tiles(const DecodeArgs& a, const int g, con
       }
       sacc = mfma_qk<QT>(ka, qb[c], sacc);
     }
+    if constexpr (kEarly && !KLDS) load(t, next);
     // Scores of tokens 4*j4 .. 4*j4+3 of the block for column n; dead ones are -inf.
-    const int tok0 = t.pos * kBlock + 4 * j4;
-    const bool reads = (t.readers & col_bit) != 0u;
+    const int tok0 = pos * kBlock + 4 * j4;
+    const bool reads = (readers_of & col_bit) != 0u;
     float sc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[r] = (reads && tok0 + r < col_end) ? sacc[r] * qk_scale : -INFINITY;
@@ -300,8 +310,8 @@ __device__ __forceinline__ void mfma_tiles(const DecodeArgs& a, const int g, con
     if constexpr (PRIO) progress_priority(k, ntiles);
 #pragma unroll
     for (int b = 0; b < NBUF; ++b) {
-      process(t[b]);
-      load(t[b], k + b + NBUF);
+      process(t[b], k + b + NBUF);
+      if constexpr (!kEarly) load(t[b], k + b + NBUF);
     }
   }
 }

@@ -150,10 +150,11 @@ def test_rows_outside_the_chunks_are_untouched():
     assert np.isfinite(o[:12]).all()
 
 
-def test_full_size_chunked_prefill_matches_oracle():
-    # The Llama-2-70B GQA chunked-prefill batch at full size, in the launch the benchmark
-    # times: every row of every sequence against the oracle.
-    cfg = PREFILL_CONFIGS["prefill_70b_gqa"]
+@pytest.mark.parametrize("name", ["prefill_70b_gqa", "prefill_70b_gqa_fp8"])
+def test_full_size_chunked_prefill_matches_oracle(name):
+    # The Llama-2-70B GQA chunked-prefill batch at full size (16-bit and fp8 caches), in the
+    # launch the benchmark times: every row of every sequence against the oracle.
+    cfg = PREFILL_CONFIGS[name]
     b = make_batch(cfg, "cuda")
     h = HostBatch(b)
     say(cfg.name, "full size")
