@@ -142,14 +142,8 @@ def gpu_bench(args, pool) -> int:
     outs = [torch.empty_like(b.q) for b in batches]
     n_pairs = len(lay.copy_pairs)
 
-    def step(i, ev=None):
+    def decode(i):   # the step's decode launch (with its reduce launch when the context is split)
         b = batches[i % len(batches)]
-        if len(b.copy_pairs):
-            pkv.copy_blocks([b.k_cache], [b.v_cache], b.copy_pairs)
-        if args.separate:
-            pkv.reshape_and_cache(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale, b.v_scale)
-        if ev is not None:
-            ev[0].record()
         if args.separate:
             pkv.paged_attention_decode(outs[i % len(batches)], b.q, b.k_cache, b.v_cache, b.block_tables,
                                        b.context_lens, b.scale, cfg.max_context_len, b.k_scale, b.v_scale,
@@ -158,6 +152,16 @@ def gpu_bench(args, pool) -> int:
             pkv.decode_step(outs[i % len(batches)], b.q, b.k_cache, b.v_cache, b.new_k, b.new_v, b.slot_mapping,
                             b.block_tables, b.context_lens, b.scale, cfg.max_context_len, b.k_scale, b.v_scale,
                             cfg.partition_size, workspace=ws)
+
+    def step(i, ev=None):
+        b = batches[i % len(batches)]
+        if len(b.copy_pairs):
+            pkv.copy_blocks([b.k_cache], [b.v_cache], b.copy_pairs)
+        if args.separate:
+            pkv.reshape_and_cache(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale, b.v_scale)
+        if ev is not None:
+            ev[0].record()
+        decode(i)
         if ev is not None:
             ev[1].record()
 
@@ -175,19 +179,36 @@ def gpu_bench(args, pool) -> int:
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     step_bytes = sum(kv_alg_r[(args.warmup + i) % len(batches)] for i in range(args.steps)) / args.steps
-    # Second pass, for the roofline: the same steps with the decode launch bracketed by
-    # events on its stream (per-launch events cost GPU time, so they stay out of the
-    # timed region above).
+    # Second pass: the decode launches of K steps alone, back to back, between two events on
+    # their stream (the step's other launches stay out; repeating a batch's decode reads the
+    # same bytes and writes the same new tokens).
+    first = args.warmup + args.steps
+    d_start = torch.cuda.Event(enable_timing=True)
+    d_end = torch.cuda.Event(enable_timing=True)
+    d_start.record()
+    for i in range(args.steps):
+        decode(first + i)
+    d_end.record()
+    torch.cuda.synchronize()
+    dec_region_ms = d_start.elapsed_time(d_end)
+    ev_bytes = sum(kv_alg_r[(first + i) % len(batches)] for i in range(args.steps))
+    # Third pass: whole steps with each decode launch between its own pair of events (each pair
+    # adds its own overhead, so these run a little longer).
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
-        step(args.warmup + args.steps + i, evs[i])
+        step(first + args.steps + i, evs[i])
     torch.cuda.synchronize()
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
     dec_avg_ms = float(dec_ms.mean())
-    first = args.warmup + args.steps
-    ev_bytes = sum(kv_alg_r[(first + i) % len(batches)] for i in range(args.steps))
-    achieved = ev_bytes / (float(dec_ms.sum()) * 1e-3) / 1e9
-    ceiling = probe_ceiling(args, cfg, batches, kv_log_r, kv_alg_r)
+    # When a step is the decode launch alone, the back-to-back pass is that launch as the timed
+    # region runs it. When a step has other launches too (copy-on-write pairs, or the separate
+    # cache write), the decode inside the step is timed by its own events instead: run alone,
+    # back to back, it can take a different time than it does inside the step.
+    alone = n_pairs == 0 and not args.separate
+    timing = "back_to_back" if alone else "per_launch_events"
+    ceiling = probe_ceiling(args, cfg, batches, kv_log_r, kv_alg_r, alone)
+    ev_bytes_pairs = sum(kv_alg_r[(first + args.steps + i) % len(batches)] for i in range(args.steps))
+    achieved = (ev_bytes / (dec_region_ms * 1e-3) if alone else ev_bytes_pairs / (float(dec_ms.sum()) * 1e-3)) / 1e9
     ceiling["frac_of_ceiling"] = round(achieved / ceiling["GBps"], 4)
 
     result = {
@@ -216,11 +237,12 @@ def gpu_bench(args, pool) -> int:
                     "copy_blocks + decode_step (cache write fused into the decode launch)",
         },
         "seqs_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
-        "decode_us": {"mean": round(dec_avg_ms * 1e3, 2), "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+        "decode_us": {"back_to_back": round(dec_region_ms / args.steps * 1e3, 2),
+                      "mean": round(dec_avg_ms * 1e3, 2), "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                       "p50": round(float(np.percentile(dec_ms, 50)) * 1e3, 2),
                       "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(cfg.name),
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "timing": timing, "traffic": load_traffic(cfg.name),
                      "kernel": "paged_decode_mfma" if cfg.group_size > 1 else "paged_decode_valu",
                      "kernel_source_hash": kernel_source_hash(), "ceiling": ceiling},
         "cpu_baseline": None,
@@ -260,10 +282,11 @@ def unique_tile_tables(cfg, lay):
     return bt, ctx
 
 
-def probe_ceiling(args, cfg, batches, kv_log_r, kv_alg_r) -> dict:
+def probe_ceiling(args, cfg, batches, kv_log_r, kv_alg_r, back_to_back) -> dict:
     """Rate of the decode read pattern alone on this device: pkv_gather_probe reads the bytes a
     decode step over each replica reads (the same tiles through the same block tables, with
-    the decode kernels' loads) and does no arithmetic. Timed like the decode launches.
+    the decode kernels' loads) and does no arithmetic. Timed like the decode launches: K
+    launches back to back between two events, or each launch between its own pair.
     Where sequences share blocks, the probe reads each group's distinct tiles once (the
     decode reads shared blocks once per group), and the rate is counted in unique bytes."""
     import torch
@@ -289,13 +312,22 @@ def probe_ceiling(args, cfg, batches, kv_log_r, kv_alg_r) -> dict:
 
     for i in range(min(args.warmup, 4)):
         run(i)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        evs[i][0].record()
-        run(i)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    if back_to_back:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            run(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = np.full(args.steps, e0.elapsed_time(e1) / args.steps)
+    else:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            evs[i][0].record()
+            run(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in evs])
     counted = kv_alg_r if shared else kv_log_r
     read = sum(counted[i % len(batches)] for i in range(args.steps))
     what = ("the distinct K/V tiles of each group of neighbouring sequences (what the decode reads once for all "
@@ -303,7 +335,7 @@ def probe_ceiling(args, cfg, batches, kv_log_r, kv_alg_r) -> dict:
         else ("the K/V tiles of every context read through the block tables with the decode kernels' "
               "loads and no arithmetic (logical bytes; pkv_gather_probe)")
     return {"kernel": "gather_probe", "GBps": round(read / (float(ms.sum()) * 1e-3) / 1e9, 1), "what": what,
-            "us": round(float(ms.mean()) * 1e3, 2)}
+            "us": round(float(ms.mean()) * 1e3, 2), "timing": "back_to_back" if back_to_back else "per_launch_events"}
 
 
 def prefill_flops(cfg, lay) -> float:
@@ -334,14 +366,18 @@ def prefill_bench(args, cfg, dev, pool) -> int:
     max_q = [int(np.diff(b.layout.query_start_loc).max()) for b in batches]
     outs = [torch.empty_like(b.q) for b in batches]
 
+    def attention(i):
+        b = batches[i % len(batches)]
+        pkv.paged_attention_prefill(outs[i % len(batches)], b.q, b.k_cache, b.v_cache, b.block_tables,
+                                    b.context_lens, b.query_start_loc, b.scale, max_q[i % len(batches)],
+                                    b.k_scale, b.v_scale)
+
     def step(i, ev=None):
         b = batches[i % len(batches)]
         pkv.reshape_and_cache(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale, b.v_scale)
         if ev is not None:
             ev[0].record()
-        pkv.paged_attention_prefill(outs[i % len(batches)], b.q, b.k_cache, b.v_cache, b.block_tables,
-                                    b.context_lens, b.query_start_loc, b.scale, max_q[i % len(batches)],
-                                    b.k_scale, b.v_scale)
+        attention(i)
         if ev is not None:
             ev[1].record()
 
@@ -357,15 +393,27 @@ def prefill_bench(args, cfg, dev, pool) -> int:
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
     step_flops = sum(flops_r[(args.warmup + i) % len(batches)] for i in range(args.steps)) / args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Roofline: the attention launches of K steps alone, back to back, between two events.
     first = args.warmup + args.steps
+    a_start = torch.cuda.Event(enable_timing=True)
+    a_end = torch.cuda.Event(enable_timing=True)
+    a_start.record()
     for i in range(args.steps):
-        step(first + i, evs[i])
+        attention(first + i)
+    a_end.record()
+    torch.cuda.synchronize()
+    pf_region_ms = a_start.elapsed_time(a_end)
+    # Whole steps with each attention launch between its own pair of events. A step also holds
+    # the chunk's cache write, so these pairs time the attention as the step runs it and give
+    # the roofline; the back-to-back figure is reported beside it.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(first + args.steps + i, evs[i])
     torch.cuda.synchronize()
     pf_ms = np.array([a.elapsed_time(b) for a, b in evs])
     pf_avg_ms = float(pf_ms.mean())
-    ev_flops = sum(flops_r[(first + i) % len(batches)] for i in range(args.steps))
-    achieved = ev_flops / (float(pf_ms.sum()) * 1e-3) / 1e12
+    ev_flops_pairs = sum(flops_r[(first + args.steps + i) % len(batches)] for i in range(args.steps))
+    achieved = ev_flops_pairs / (float(pf_ms.sum()) * 1e-3) / 1e12
     kernel, sources = prefill_kernel(cfg.kv_dtype)
     result = {
         "metric": "paged prefill-chunk attention: achieved matrix TFLOP/s (% of dense bf16 peak) and tokens/s",
@@ -390,11 +438,11 @@ def prefill_bench(args, cfg, dev, pool) -> int:
             "step": "reshape_and_cache (chunk) + paged_attention_prefill",
         },
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
-        "prefill_us": {"mean": round(pf_avg_ms * 1e3, 2), "p10": round(float(np.percentile(pf_ms, 10)) * 1e3, 2),
+        "prefill_us": {"back_to_back": round(pf_region_ms / args.steps * 1e3, 2), "mean": round(pf_avg_ms * 1e3, 2), "p10": round(float(np.percentile(pf_ms, 10)) * 1e3, 2),
                        "p50": round(float(np.percentile(pf_ms, 50)) * 1e3, 2),
                        "p90": round(float(np.percentile(pf_ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                     "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), "timing": "per_launch_events",
                      "traffic": load_traffic(cfg.name, "prefill", sources),
                      "kernel": kernel, "kernel_source_hash": kernel_source_hash(sources)},
         "cpu_baseline": None,
