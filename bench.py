@@ -8,9 +8,10 @@
 
 A step is the whole hot path over one synthetic batch: copy-on-write block copies
 (when the batch has any), the cache write of every sequence's new token, then
-decode attention over the paged cache; the write and the attention run as one
-launch (pkv_decode_step; --separate times the two launches instead). Inputs are
-resident in HBM before timing.
+decode attention over the paged cache. All three run as one launch (pkv_decode_step
+with cow_src); --cow-launch copies with copy_blocks first, and --separate times
+copy_blocks, reshape_and_cache and paged_attention_decode as three launches. Inputs
+are resident in HBM before timing.
 Consecutive steps rotate over --replicas independent batches (own pools and block
 tables), so each step reads KV bytes the previous steps did not touch: about 2 GB
 lie between two reads of the same batch, far beyond the 256 MB last-level cache.
@@ -88,6 +89,9 @@ def main() -> int:
     ap.add_argument("--cpu-sample-seqs", type=int, default=0, help="sequences the oracle times (0: auto)")
     ap.add_argument("--separate", action="store_true",
                     help="write the new tokens with their own launch instead of inside the decode launch")
+    ap.add_argument("--cow-launch", action="store_true",
+                    help="copy the step's copy-on-write pairs with copy_blocks before the decode launch instead "
+                         "of inside it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -142,6 +146,10 @@ def gpu_bench(args, pool) -> int:
     outs = [torch.empty_like(b.q) for b in batches]
     n_pairs = len(lay.copy_pairs)
 
+    # Copy-on-write: fused into the decode launch (cow_src) unless the step is timed in its
+    # separate-launch forms (--separate, --cow-launch), where copy_blocks runs first.
+    copy_launch = n_pairs > 0 and (args.separate or args.cow_launch)
+
     def decode(i):   # the step's decode launch (with its reduce launch when the context is split)
         b = batches[i % len(batches)]
         if args.separate:
@@ -151,11 +159,12 @@ def gpu_bench(args, pool) -> int:
         else:
             pkv.decode_step(outs[i % len(batches)], b.q, b.k_cache, b.v_cache, b.new_k, b.new_v, b.slot_mapping,
                             b.block_tables, b.context_lens, b.scale, cfg.max_context_len, b.k_scale, b.v_scale,
-                            cfg.partition_size, workspace=ws)
+                            cfg.partition_size, workspace=ws,
+                            cow_src=None if (copy_launch or n_pairs == 0) else b.cow_src)
 
     def step(i, ev=None):
         b = batches[i % len(batches)]
-        if len(b.copy_pairs):
+        if copy_launch and len(b.copy_pairs):
             pkv.copy_blocks([b.k_cache], [b.v_cache], b.copy_pairs)
         if args.separate:
             pkv.reshape_and_cache(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale, b.v_scale)
@@ -204,7 +213,7 @@ def gpu_bench(args, pool) -> int:
     # region runs it. When a step has other launches too (copy-on-write pairs, or the separate
     # cache write), the decode inside the step is timed by its own events instead: run alone,
     # back to back, it can take a different time than it does inside the step.
-    alone = n_pairs == 0 and not args.separate
+    alone = not copy_launch and not args.separate
     timing = "back_to_back" if alone else "per_launch_events"
     ceiling = probe_ceiling(args, cfg, batches, kv_log_r, kv_alg_r, alone)
     ev_bytes_pairs = sum(kv_alg_r[(first + args.steps + i) % len(batches)] for i in range(args.steps))
@@ -234,7 +243,9 @@ def gpu_bench(args, pool) -> int:
             "copy_pairs": n_pairs,
             "replicas": args.replicas, "seed": cfg.seed, "parallelism": "single GPU",
             "step": "copy_blocks + reshape_and_cache + paged_attention_decode" if args.separate else
-                    "copy_blocks + decode_step (cache write fused into the decode launch)",
+                    ("copy_blocks + decode_step (cache write fused into the decode launch)" if copy_launch else
+                     "decode_step (cache write, and copy-on-write of the step's pairs via cow_src, fused into the "
+                     "decode launch)"),
         },
         "seqs_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
         "decode_us": {"back_to_back": round(dec_region_ms / args.steps * 1e3, 2),

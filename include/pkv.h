@@ -62,7 +62,8 @@
 extern "C" {
 #endif
 
-#define PKV_API_VERSION 1
+/* 2: pkv_decode_step and pkv_decode_step_no_alloc take cow_src. */
+#define PKV_API_VERSION 2
 
 /* Element types. */
 typedef enum pkv_dtype {
@@ -170,12 +171,22 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
  *   slot_mapping   [num_seqs] int64: slot of sequence s's new token, which must be the slot
  *                  of its logical position context_lens[s] - 1 in its own (unshared)
  *                  blocks; a negative slot is skipped
- *   k_cache/v_cache written (new tokens, converted as pkv_reshape_and_cache does, fp8
+ *   cow_src        [num_seqs] int32 or NULL: copy-on-write ("vLLM推理引擎PagedAttention原理
+ *                  与性能优化实战", §3.2: the first write into a block that several
+ *                  sequences share goes to a private copy). cow_src[s] >= 0 makes the block
+ *                  that holds sequence s's last position (its block-table entry, private to
+ *                  s) a copy of block cow_src[s], for this cache's K and V, before s's new
+ *                  token is written into it: the results are those of
+ *                  pkv_copy_blocks(pairs (cow_src[s], that block)) followed by the two calls
+ *                  above, bit for bit. -1 (or an id outside the pool) copies nothing. No
+ *                  other sequence may read the destination block in the same step.
+ *   k_cache/v_cache written (copies, new tokens converted as pkv_reshape_and_cache does, fp8
  *                  with k_scale / v_scale) and read
  * Every other argument is as for pkv_paged_attention_decode, whose checks also apply.
+ * Returns PKV_ERR_ALIGN for a cow_src that is not 4-byte aligned.
  */
 int pkv_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
-                    const void* key, const void* value, const int64_t* slot_mapping,
+                    const void* key, const void* value, const int64_t* slot_mapping, const int32_t* cow_src,
                     const int32_t* block_tables, const int32_t* context_lens,
                     int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                     int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
@@ -208,7 +219,7 @@ int pkv_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
  * (the current device for NULL).
  */
 int pkv_decode_step_no_alloc(void* out, const void* q, void* k_cache, void* v_cache,
-                             const void* key, const void* value, const int64_t* slot_mapping,
+                             const void* key, const void* value, const int64_t* slot_mapping, const int32_t* cow_src,
                              const int32_t* block_tables, const int32_t* context_lens,
                              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                              int64_t num_blocks, int max_blocks_per_seq, int max_context_len,

@@ -141,6 +141,7 @@ struct NewTokens {
   const void* value;
   const int64_t* slot_mapping;
   int64_t key_stride, value_stride;
+  const int32_t* cow_src;   // may be null
 };
 
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -185,6 +186,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     return PKV_ERR_ALIGN;
   if (tok && (!aligned16(tok->key) || !aligned16(tok->value) || key_stride % 8 != 0 || value_stride % 8 != 0))
     return PKV_ERR_ALIGN;
+  if (tok && reinterpret_cast<uintptr_t>(tok->cow_src) % alignof(int32_t) != 0) return PKV_ERR_ALIGN;
 
   Plan plan;
   const int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size, &plan);
@@ -251,6 +253,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.new_key = tok ? tok->key : nullptr;
   a.new_value = tok ? tok->value : nullptr;
   a.slot_mapping = tok ? tok->slot_mapping : nullptr;
+  a.cow_src = tok ? tok->cow_src : nullptr;
   a.key_stride = key_stride;
   a.value_stride = value_stride;
   a.num_slots = num_blocks * block_size;
@@ -297,14 +300,14 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
 }
 
 int pkv_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
-                    const void* key, const void* value, const int64_t* slot_mapping,
+                    const void* key, const void* value, const int64_t* slot_mapping, const int32_t* cow_src,
                     const int32_t* block_tables, const int32_t* context_lens,
                     int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                     int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
                     int q_dtype, int kv_dtype, float scale, float k_scale, float v_scale,
                     int64_t q_seq_stride, int64_t key_stride, int64_t value_stride, int partition_size,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  const NewTokens tok{key, value, slot_mapping, key_stride, value_stride};
+  const NewTokens tok{key, value, slot_mapping, key_stride, value_stride, cow_src};
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, scale,
                      k_scale, v_scale, q_seq_stride, partition_size, &tok, workspace, workspace_bytes, stream);
@@ -350,7 +353,7 @@ int scratch_address(hipStream_t stream, void** out) {
 extern "C" {
 
 int pkv_decode_step_no_alloc(void* out, const void* q, void* k_cache, void* v_cache,
-                             const void* key, const void* value, const int64_t* slot_mapping,
+                             const void* key, const void* value, const int64_t* slot_mapping, const int32_t* cow_src,
                              const int32_t* block_tables, const int32_t* context_lens,
                              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                              int64_t num_blocks, int max_blocks_per_seq, int max_context_len,
@@ -360,7 +363,7 @@ int pkv_decode_step_no_alloc(void* out, const void* q, void* k_cache, void* v_ca
   void* ws = nullptr;
   const int st = scratch_address(reinterpret_cast<hipStream_t>(stream), &ws);
   if (st != PKV_OK) return st;
-  const NewTokens tok{key, value, slot_mapping, key_stride, value_stride};
+  const NewTokens tok{key, value, slot_mapping, key_stride, value_stride, cow_src};
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, scale,
                      k_scale, v_scale, q_seq_stride, partition_size, &tok, ws, PKV_NO_ALLOC_SCRATCH_BYTES, stream);

@@ -34,6 +34,9 @@ struct DecodeArgs {
   const void* new_key;            // [S, Hkv, D] q dtype, token stride key_stride elements
   const void* new_value;          // [S, Hkv, D] q dtype, token stride value_stride elements
   const int64_t* slot_mapping;    // [S]: slot of each new token; negative = no write
+  // Fused step with copy-on-write (nullptr: none): cow_src[s] >= 0 names the block that the
+  // block holding sequence s's last position becomes a copy of before the new token is written.
+  const int32_t* cow_src;         // [S]
   int64_t key_stride, value_stride;
   int64_t num_slots;              // num_blocks * block size
   float k_quant, v_quant;         // fp8 scales the new values are divided by
@@ -143,24 +146,66 @@ __device__ __forceinline__ void prefetch_bt_slice(const DecodeArgs& a, int s, in
     sl.v[k] = tile_name(row, t0 + min(k * kWave + lane, hi - 1), a.block_shift, a.num_blocks);
 }
 
+// Copy-on-write in the fused step ("vLLM推理引擎PagedAttention原理与性能优化实战", §3.2: the
+// first write into a block that several sequences share goes to a private copy of it). When
+// cow_src[s] names a block, the block that holds sequence s's last position (block `lb` of
+// its table, `dst`, private to s) is to become a copy of block `src` before the new token
+// lands in it. Within the step that block still holds stale bytes: its tiles are read from
+// `src` instead (the new token's row is patched in as always), and the work item that
+// writes the new token also copies `src` into `dst`, every row but the token's (`skip`).
+// A source or destination outside the pool, or a block copied onto itself, copies nothing.
+struct CowRead {
+  int lb;     // logical block of the sequence's last position
+  int src;    // its source block, -1: no copy
+  int dst;    // the block-table entry lb
+  int skip;   // row of dst the new token is written to, -1: none
+};
+
+__device__ __forceinline__ CowRead cow_read(const DecodeArgs& a, int s, int ctx) {
+  CowRead c{-1, -1, -1, -1};
+  if (a.cow_src == nullptr || ctx <= 0) return c;
+  const int b = a.cow_src[s];
+  const int P = kBlock << a.block_shift;
+  const int lb = (ctx - 1) / P;
+  const int dst = a.block_tables[(int64_t)s * a.max_blocks + lb];
+  if (b >= 0 && b < a.num_blocks && dst >= 0 && dst < a.num_blocks && dst != b) {
+    const int64_t slot = a.slot_mapping[s];
+    c.lb = lb;
+    c.src = b;
+    c.dst = dst;
+    c.skip = (slot >= 0 && slot < a.num_slots && slot / P == dst) ? (int)(slot % P) : -1;
+  }
+  return c;
+}
+
+// The name of 16-token tile tt (whose name in the block table is `name`) as the step reads it.
+__device__ __forceinline__ int cow_tile(const CowRead& c, int tt, int shift, int name) {
+  return (c.src >= 0 && (tt >> shift) == c.lb) ? c.src * (1 << shift) + (tt & ((1 << shift) - 1)) : name;
+}
+
 // Stores entries [0, n) of the slice of sequence s from tile t0 into dst (n <= the
 // prefetch bound): the prefetched ones, then any further ones, eight loads in flight per
-// lane (indices past n re-read entry n - 1 and are not stored).
+// lane (indices past n re-read entry n - 1 and are not stored). Tiles of a copy-on-write
+// block are stored under their source's name (`cow`).
 __device__ __forceinline__ void store_bt_slice(const DecodeArgs& a, int s, int t0, int n, const BtSlice& sl,
-                                               int* dst) {
-  const int lane = threadIdx.x & (kWave - 1);
+                                               int* dst, const CowRead& cow) {
+  const int lane = threadIdx.x & (kWave - 1), shift = a.block_shift;
 #pragma unroll
-  for (int k = 0; k < kBtBatch; ++k)
-    if (k * kWave + lane < n) dst[k * kWave + lane] = sl.v[k];
+  for (int k = 0; k < kBtBatch; ++k) {
+    const int i = k * kWave + lane;
+    if (i < n) dst[i] = cow_tile(cow, t0 + i, shift, sl.v[k]);
+  }
   const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks;
   for (int i0 = kBtBatch * kWave; i0 < n; i0 += kBtBatch * kWave) {
     int v[kBtBatch];
 #pragma unroll
     for (int k = 0; k < kBtBatch; ++k)
-      v[k] = tile_name(row, t0 + min(i0 + k * kWave + lane, n - 1), a.block_shift, a.num_blocks);
+      v[k] = tile_name(row, t0 + min(i0 + k * kWave + lane, n - 1), shift, a.num_blocks);
 #pragma unroll
-    for (int k = 0; k < kBtBatch; ++k)
-      if (i0 + k * kWave + lane < n) dst[i0 + k * kWave + lane] = v[k];
+    for (int k = 0; k < kBtBatch; ++k) {
+      const int i = i0 + k * kWave + lane;
+      if (i < n) dst[i] = cow_tile(cow, t0 + i, shift, v[k]);
+    }
   }
 }
 
@@ -234,6 +279,97 @@ __device__ __forceinline__ void stage_new_token(const TokenChunk& t, uint8_t* ro
 template <int KVT>
 __device__ __forceinline__ void store_new_token(const DecodeArgs& a, const TokenChunk& t) {
   if (t.store) store_converted_chunk<KVT>(t.data, const_cast<void*>(t.is_v ? a.v_cache : a.k_cache), t.dst);
+}
+
+// A work item keeps its sequence's CowRead in LDS (at kCowSlot of the sequence's token-row
+// area, after the new token's two rows of up to 256 bytes each) from its start to the copy
+// at its end, rather than in registers across its tile loop.
+constexpr int kCowSlot = 512;
+__device__ __forceinline__ void stash_cow(uint8_t* tok_rows, const CowRead& c) {
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    int* slot = (int*)(tok_rows + kCowSlot);
+    slot[0] = c.lb;
+    slot[1] = c.src;
+    slot[2] = c.dst;
+    slot[3] = c.skip;
+  }
+}
+__device__ __forceinline__ CowRead stashed_cow(const uint8_t* tok_rows) {
+  const int* slot = (const int*)(tok_rows + kCowSlot);
+  return CowRead{slot[0], slot[1], slot[2], slot[3]};
+}
+
+// The copy of a copy-on-write block for kv head g, by one wavefront: kv head g's slice of
+// block cow.src is copied, K and V, into block cow.dst, except row cow.skip, in 16-byte
+// chunks (chunk c: tensor c / chunks, byte 16 (c mod chunks) of the slice). Done by the
+// work item that writes the sequence's new token, after its tiles. cow_copy_begin loads the
+// lane's first CowChunks<D>::kBatch chunks and cow_copy_end stores them and copies any further chunks:
+// the group mode puts its merge between the two, which hides the loads' latency; the other
+// paths call cow_copy (both at once). Nothing else in the launch reads the destination
+// block.
+// Chunks per lane that cow_copy_begin loads: a 16-token fp8 block's slice at D = 128, half of
+// it at D = 64 (where four would cost the matrix-core kernel a wavefront per SIMD).
+template <int D>
+struct CowChunks {
+  static constexpr int kBatch = D >= 128 ? 4 : 2;
+  u32x4 v[kBatch];
+};
+
+template <int KVT, int D>
+struct CowGeometry {
+  static constexpr int kRB = row_bytes<KVT, D>();
+  int chunks;            // 16-byte chunks per tensor
+  int64_t src_off, dst_off;
+  __device__ __forceinline__ CowGeometry(const DecodeArgs& a, int g, const CowRead& cow) {
+    const int P = kBlock << a.block_shift;
+    const int64_t slice = (int64_t)P * kRB;   // one kv head's share of a block
+    chunks = P * kRB / 16;
+    src_off = ((int64_t)cow.src * a.num_kv_heads + g) * slice;
+    dst_off = ((int64_t)cow.dst * a.num_kv_heads + g) * slice;
+  }
+  __device__ __forceinline__ uint8_t* base(const DecodeArgs& a, int c) const {
+    return (uint8_t*)const_cast<void*>(c >= chunks ? a.v_cache : a.k_cache);
+  }
+  __device__ __forceinline__ int64_t off(int c) const { return (int64_t)(c >= chunks ? c - chunks : c) * 16; }
+  __device__ __forceinline__ bool skipped(int c, int skip) const {
+    return (int)(off(c) / kRB) == skip;
+  }
+};
+
+template <int KVT, int D>
+__device__ __forceinline__ void cow_copy_begin(const DecodeArgs& a, int g, const CowRead& cow, CowChunks<D>& ch) {
+  if (cow.src < 0) return;
+  const CowGeometry<KVT, D> geo(a, g, cow);
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int k = 0; k < CowChunks<D>::kBatch; ++k) {
+    const int c = lane + k * kWave;
+    if (c < 2 * geo.chunks) ch.v[k] = *(const u32x4*)(geo.base(a, c) + geo.src_off + geo.off(c));
+  }
+}
+
+template <int KVT, int D>
+__device__ __forceinline__ void cow_copy_end(const DecodeArgs& a, int g, const CowRead& cow, const CowChunks<D>& ch) {
+  if (cow.src < 0) return;
+  const CowGeometry<KVT, D> geo(a, g, cow);
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int k = 0; k < CowChunks<D>::kBatch; ++k) {
+    const int c = lane + k * kWave;
+    if (c < 2 * geo.chunks && !geo.skipped(c, cow.skip)) *(u32x4*)(geo.base(a, c) + geo.dst_off + geo.off(c)) = ch.v[k];
+  }
+  for (int c = lane + CowChunks<D>::kBatch * kWave; c < 2 * geo.chunks; c += kWave) {
+    if (geo.skipped(c, cow.skip)) continue;
+    const u32x4 x = *(const u32x4*)(geo.base(a, c) + geo.src_off + geo.off(c));
+    *(u32x4*)(geo.base(a, c) + geo.dst_off + geo.off(c)) = x;
+  }
+}
+
+template <int KVT, int D>
+__device__ __forceinline__ void cow_copy(const DecodeArgs& a, int g, const CowRead& cow) {
+  CowChunks<D> ch;
+  cow_copy_begin<KVT, D>(a, g, cow, ch);
+  cow_copy_end<KVT, D>(a, g, cow, ch);
 }
 
 // Replaces the bytes a lane loaded for one 16-byte piece of a tile with the new token's

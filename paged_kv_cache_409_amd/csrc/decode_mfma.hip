@@ -366,7 +366,11 @@ __device__ __forceinline__ void mfma_single(const DecodeArgs& a, const int s, co
   const int G = a.group;
   const int end = min(ctx, start + a.part_blocks * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
-  store_bt_slice(a, s, start / kBlock, nblk, sl, bt_lds);
+  {
+    const CowRead cow = cow_read(a, s, ctx);
+    stash_cow(tok_rows, cow);
+    store_bt_slice(a, s, start / kBlock, nblk, sl, bt_lds, cow);
+  }
   if (writes) stage_new_token<KVT, D>(token, tok_rows);
   u32x4 qb[D / 32];
   load_q<QT, KVT, D>(a, n < G, s, g * G + n, qb);
@@ -383,7 +387,10 @@ __device__ __forceinline__ void mfma_single(const DecodeArgs& a, const int s, co
                                                           writes && token.written ? (ctx - 1) / kBlock : -1,
                                                           (ctx - 1) % kBlock,
                                                           nullptr, nullptr, tok_rows);
-  if (writes) store_new_token<KVT>(a, token);
+  if (writes) {
+    store_new_token<KVT>(a, token);
+    cow_copy<KVT, D>(a, g, stashed_cow(tok_rows));
+  }
   const float l_tot = sum_xor32(sum_xor16(st.l));
   if (n < G) write_column<QT, D>(a, s, g * G + n, p, st.o, st.m, l_tot);
 }
@@ -419,7 +426,10 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
   if (writes && !token_loaded) token = load_new_token<QT, KVT, D>(a, s, g);
   const int end = min(ctx, start + PB * kBlock);
   const int nblk = (end - start + kBlock - 1) / kBlock;
-  store_bt_slice(a, s, start / kBlock, nblk, sl, bts + w * PB);
+  // The slices keep the block table's names, which decide which tiles the sequences share (a
+  // copy-on-write block is private to its sequence); the list names the source instead.
+  store_bt_slice(a, s, start / kBlock, nblk, sl, bts + w * PB, CowRead{-1, -1, -1, -1});
+  stash_cow(tok_rows + w * kTokenRowsLds, cow_read(a, s, ctx));
   if (lane == 0) {
     ends[w] = end;
     patch_pos[w] = writes && token.written ? (ctx - 1) / kBlock : -1;
@@ -502,6 +512,17 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
       ntiles += total;
     }
   }
+  // Copy-on-write: an entry whose only reader has its last block copied names the source.
+  // (The pass runs in every step: testing for copy-on-write here would keep its pointer live.)
+  wave_lds_sync();
+  for (int e = lane; e < ntiles; e += kWave) {
+    const int meta = my_meta[e];
+    const uint32_t rd = (uint32_t)(meta >> 16) & 0xFFu;
+    if (rd != 0u && (rd & (rd - 1u)) == 0u) {
+      const CowRead c = stashed_cow(tok_rows + __builtin_ctz(rd) * kTokenRowsLds);
+      if (c.src >= 0) my_id[e] = cow_tile(c, meta & 0xFFFF, a.block_shift, my_id[e]);
+    }
+  }
   wave_lds_sync();
 
   // 3. The wave's tiles, for all of the group's columns (two tiles in flight, default issue
@@ -516,7 +537,14 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
                                                              col_ok ? (1u << cb) : 0u, col_ok ? ends[cb] : 0,
                                                              tiles + w * Tr::kLdsBytes, st, -1, 0,
                                                              patch_pos, patch_row, tok_rows);
-  if (writes) store_new_token<KVT>(a, token);
+  // Copy-on-write: the source's bytes are requested now and stored after the merge below.
+  CowRead cow{-1, -1, -1, -1};
+  CowChunks<D> cow_chunks;
+  if (writes) {
+    cow = stashed_cow(tok_rows + w * kTokenRowsLds);
+    cow_copy_begin<KVT, D>(a, g, cow, cow_chunks);
+    store_new_token<KVT>(a, token);
+  }
   const float l_w = sum_xor32(sum_xor16(st.l));
 
   // 4. Merge the waves' states column by column (the tile staging area is free again). The
@@ -531,6 +559,7 @@ __device__ __forceinline__ void mfma_group(const DecodeArgs& a, const int s0, co
     merge_ml[(w * 16 + n) * 2 + 1] = l_w;
   }
   __syncthreads();
+  if (writes) cow_copy_end<KVT, D>(a, g, cow, cow_chunks);
   if (!col_ok) return;
   float M = -INFINITY;
   for (int v = 0; v < B; ++v) M = fmaxf(M, merge_ml[(v * 16 + n) * 2]);

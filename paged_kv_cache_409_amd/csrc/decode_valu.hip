@@ -121,7 +121,11 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, co
       qv[x] = w[0]; qv[x + 1] = w[1]; qv[x + 2] = w[2]; qv[x + 3] = w[3];
     }
   }
-  store_bt_slice(a, it.s, start / kBlock, nblk, sl, bt_lds);
+  {
+    const CowRead cow = cow_read(a, it.s, ctx);
+    stash_cow(tok_rows, cow);
+    store_bt_slice(a, it.s, start / kBlock, nblk, sl, bt_lds, cow);
+  }
   if (writes) stage_new_token<KVT, D>(token, tok_rows);
   __syncthreads();
   // Fused step: the tile of the new token (the sequence's last position, ctx - 1) gets the
@@ -219,7 +223,10 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const Item it, co
     }
   }
 
-  if (writes) store_new_token<KVT>(a, token);
+  if (writes) {
+    store_new_token<KVT>(a, token);
+    cow_copy<KVT, D>(a, it.g, stashed_cow(tok_rows));
+  }
 
   // Combine the row groups.
   const float l_tot = groups_sum<LPR>(l_run);

@@ -37,8 +37,10 @@ constexpr int kDecodeSmallLds = 2048;
 // workgroup stages in LDS.
 constexpr int kMaxGroupListEntries = 2048;
 
-// LDS copy of one sequence's new token (K row then V row, storage format) in a fused step.
-constexpr int kTokenRowsLds = 512;
+// Per sequence in a fused step: the LDS copy of its new token (K row then V row, storage
+// format, up to 512 bytes) and, at byte kCowSlot (decode_common.h), its copy-on-write block
+// and source.
+constexpr int kTokenRowsLds = kCowSlot + 16;
 
 // Entries reserved per wavefront for its group-mode tile list: a wave lists every B-th
 // logical block of the partition, each with up to B distinct physical blocks, so at most

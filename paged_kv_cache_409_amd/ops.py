@@ -142,18 +142,31 @@ def _step_checks(out, q, k_cache, v_cache, key, value, slot_mapping, block_table
     return S, Hq, Hkv, D, P, NB
 
 
+def _cow_ptr(cow_src, S: int):
+    """Device address of the per-sequence copy-on-write sources (int32 [num_seqs]), or None."""
+    if cow_src is None:
+        return None
+    _dev(cow_src)
+    if cow_src.dtype != torch.int32 or tuple(cow_src.shape) != (S,):
+        raise ValueError("cow_src must be int32 [num_seqs]")
+    return cow_src.data_ptr()
+
+
 def decode_step(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens, scale: float,
                 max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
-                workspace: torch.Tensor | None = None, stream=None):
+                workspace: torch.Tensor | None = None, stream=None, cow_src: torch.Tensor | None = None):
     """Cache write of every sequence's new token, then decode attention, in one launch
-    (same results as reshape_and_cache followed by paged_attention_decode)."""
+    (same results as reshape_and_cache followed by paged_attention_decode). With cow_src
+    (int32 [num_seqs], -1: none), the block holding sequence s's last position first becomes
+    a copy of block cow_src[s] (same results as copy_blocks of those pairs beforehand)."""
     S, Hq, Hkv, D, P, NB = _step_checks(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables,
                                         context_lens)
+    cow = _cow_ptr(cow_src, S)
     ws_ptr, ws_bytes = _workspace(workspace, workspace_size(S, Hq, Hkv, D, max_context_len, partition_size),
                                   q.device)
     st = _lib.load().pkv_decode_step(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), key.data_ptr(), value.data_ptr(),
-        slot_mapping.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, Hq, Hkv, D, P, NB,
+        slot_mapping.data_ptr(), cow, block_tables.data_ptr(), context_lens.data_ptr(), S, Hq, Hkv, D, P, NB,
         block_tables.shape[1], max_context_len, _dtype(q), _dtype(k_cache), scale, k_scale, v_scale, 0, 0, 0,
         partition_size, ws_ptr, ws_bytes, _stream(stream))
     _check("pkv_decode_step", st)
@@ -162,15 +175,16 @@ def decode_step(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables
 
 def decode_step_no_alloc(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens,
                          scale: float, max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0,
-                         partition_size: int = 0, stream=None):
+                         partition_size: int = 0, stream=None, cow_src: torch.Tensor | None = None):
     """decode_step without a workspace and without any allocation, by this binding or the
     library: split-context partials go to the library's fixed scratch array of the GPU
     (see pkv_decode_step_no_alloc; calls that overlap in time on one GPU race)."""
     S, Hq, Hkv, D, P, NB = _step_checks(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables,
                                         context_lens)
+    cow = _cow_ptr(cow_src, S)
     st = _lib.load().pkv_decode_step_no_alloc(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), key.data_ptr(), value.data_ptr(),
-        slot_mapping.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, Hq, Hkv, D, P, NB,
+        slot_mapping.data_ptr(), cow, block_tables.data_ptr(), context_lens.data_ptr(), S, Hq, Hkv, D, P, NB,
         block_tables.shape[1], max_context_len, _dtype(q), _dtype(k_cache), scale, k_scale, v_scale, 0, 0, 0,
         partition_size, _stream(stream))
     _check("pkv_decode_step_no_alloc", st)

@@ -86,7 +86,7 @@ def device_batch(cfg: WorkloadConfig, replica: int = 0):
     """Small configs: draw on the CPU (reproducible everywhere), then move to the GPU."""
     b = make_batch(cfg, "cpu", replica)
     for name in ("q", "new_k", "new_v", "k_cache", "v_cache", "block_tables", "context_lens", "slot_mapping",
-                 "copy_pairs", "query_start_loc"):
+                 "copy_pairs", "query_start_loc", "cow_src"):
         setattr(b, name, getattr(b, name).cuda())
     return b
 
@@ -99,6 +99,16 @@ def gpu_fused_step(b, partition_size=None):
     part = b.cfg.partition_size if partition_size is None else partition_size
     pkv.decode_step(out, b.q, b.k_cache, b.v_cache, b.new_k, b.new_v, b.slot_mapping, b.block_tables, b.context_lens,
                     b.scale, b.cfg.max_context_len, b.k_scale, b.v_scale, part)
+    return out
+
+
+def gpu_cow_step(b, partition_size=None, no_alloc=False, cow_src=None):
+    """The same step with the copy-on-write copies fused into the decode launch too (cow_src)."""
+    out = torch.empty_like(b.q)
+    part = b.cfg.partition_size if partition_size is None else partition_size
+    step = pkv.decode_step_no_alloc if no_alloc else pkv.decode_step
+    step(out, b.q, b.k_cache, b.v_cache, b.new_k, b.new_v, b.slot_mapping, b.block_tables, b.context_lens,
+         b.scale, b.cfg.max_context_len, b.k_scale, b.v_scale, part, cow_src=b.cow_src if cow_src is None else cow_src)
     return out
 
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    assert lib.pkv_api_version() == 1
+    assert lib.pkv_api_version() == _lib.API_VERSION == 2
     for code in range(0, -8, -1):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(-99) == b"unknown status"
@@ -107,9 +107,9 @@ def test_fused_step_argument_errors():
     lib = _lib.load()
 
     def step(**kw):
-        a = dict(key=16, value=16, slots=16, kstride=0, vstride=0, S=4, Hq=8, Hkv=2)
+        a = dict(key=16, value=16, slots=16, cow=None, kstride=0, vstride=0, S=4, Hq=8, Hkv=2)
         a.update(kw)
-        return lib.pkv_decode_step(16, 16, 16, 16, a["key"], a["value"], a["slots"], 16, 16, a["S"], a["Hq"],
+        return lib.pkv_decode_step(16, 16, 16, 16, a["key"], a["value"], a["slots"], a["cow"], 16, 16, a["S"], a["Hq"],
                                    a["Hkv"], 128, 16, 64, 4, 64, _lib.PKV_BF16, _lib.PKV_BF16, 0.1, 1.0, 1.0, 0,
                                    a["kstride"], a["vstride"], 0, None, 0, None)
     assert step(key=None) == -1
@@ -117,6 +117,8 @@ def test_fused_step_argument_errors():
     assert step(value=8) == -6                 # misaligned
     assert step(kstride=100) == -2             # shorter than one token's rows (2 * 128)
     assert step(kstride=260) == -6             # not a multiple of 8 elements
+    assert step(cow=18) == -6                  # copy-on-write sources not 4-byte aligned
+    assert step(cow=20, S=0) == 0
     assert step(Hq=7) == -2
     assert step(S=0) == 0
 

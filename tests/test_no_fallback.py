@@ -35,3 +35,12 @@ def test_host_or_strided_workspace_is_refused():
     with pytest.raises(ValueError, match="device tensors"):
         ops._workspace(torch.zeros(256, dtype=torch.float32), 512, "cpu")
     assert ops._workspace(None, 0, "cpu") == (None, 0)
+
+
+def test_host_copy_on_write_sources_are_refused():
+    # cow_src is read by the kernels: the binding takes only an int32 [num_seqs] device
+    # tensor (checked before any library call; no GPU here, so a host tensor is refused).
+    from paged_kv_cache_409_amd import ops
+    assert ops._cow_ptr(None, 4) is None
+    with pytest.raises(ValueError, match="device tensors"):
+        ops._cow_ptr(torch.full((4,), -1, dtype=torch.int32), 4)

@@ -53,6 +53,8 @@ class Layout:
     history_valid: np.ndarray     # bool [NB, P], slots holding KV before the step
     poison_block: int
     query_start_loc: np.ndarray   # int32 [S + 1]: sequence s's new tokens are rows [qsl[s], qsl[s+1])
+    cow_src: np.ndarray           # int32 [S]: source of the copy-on-write pair whose destination is
+                                  # the block sequence s writes into this step, -1: none
 
 
 def _seed_streams(cfg: WorkloadConfig, replica: int, n: int):
@@ -134,12 +136,14 @@ def make_layout(cfg: WorkloadConfig, replica: int = 0) -> Layout:
     query_start_loc[1:] = np.cumsum(new_tokens)
     slot_mapping = np.empty(int(query_start_loc[-1]), dtype=np.int64)
     pairs = []
+    cow_src = np.full(S, -1, dtype=np.int32)
     for i, seq in enumerate(live):
         for k in range(int(new_tokens[i])):
             slot, copy = seq.append_slot()
             slot_mapping[query_start_loc[i] + k] = slot
             if copy is not None:
                 pairs.append(copy)
+                cow_src[i] = copy[0]
     block_tables = np.full((S, cfg.max_blocks_per_seq), poison, dtype=np.int32)
     context_lens = np.empty(S, dtype=np.int32)
     for i, seq in enumerate(live):
@@ -149,7 +153,7 @@ def make_layout(cfg: WorkloadConfig, replica: int = 0) -> Layout:
         context_lens[i] = seq.num_tokens
     copy_pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
     return Layout(block_tables, context_lens, slot_mapping, copy_pairs,
-                  valid.reshape(cfg.num_blocks, P), poison, query_start_loc)
+                  valid.reshape(cfg.num_blocks, P), poison, query_start_loc, cow_src)
 
 
 @dataclass
@@ -167,6 +171,7 @@ class Batch:
     slot_mapping: torch.Tensor   # int64 [T]
     copy_pairs: torch.Tensor     # int64 [Pn, 2]
     query_start_loc: torch.Tensor  # int32 [S + 1]
+    cow_src: torch.Tensor        # int32 [S]
 
     @property
     def scale(self) -> float:
@@ -226,7 +231,7 @@ def make_batch(cfg: WorkloadConfig, device="cpu", replica: int = 0) -> Batch:
     v_cache = make_pool(cfg, lay.history_valid, device, base + 5)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
     return Batch(cfg, lay, q, new_k, new_v, k_cache, v_cache, t(lay.block_tables), t(lay.context_lens),
-                 t(lay.slot_mapping), t(lay.copy_pairs), t(lay.query_start_loc))
+                 t(lay.slot_mapping), t(lay.copy_pairs), t(lay.query_start_loc), t(lay.cow_src))
 
 
 def kv_bytes_logical(cfg: WorkloadConfig, context_lens) -> int:
