@@ -80,6 +80,14 @@ int pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens, 
 int pkv_bm_append_batch(pkv_block_manager* bm, const int64_t* seq_ids, int n, const int32_t* tokens,
                         int64_t* slots_out, int64_t* cow_pairs, int cow_cap, int* num_cow);
 
+/*
+ * pkv_bm_append_batch for pkv_decode_step's fused copy-on-write: the same appends, with
+ * sequence i's copy-on-write source in cow_src_out[i] (int32; the pair's `old` block, whose
+ * copy is the block its new token lands in; -1 when it needs no copy) in place of a pair list.
+ */
+int pkv_bm_append_step(pkv_block_manager* bm, const int64_t* seq_ids, int n, const int32_t* tokens,
+                       int64_t* slots_out, int32_t* cow_src_out);
+
 /* child_id shares every block of parent_id (which must be on the GPU). */
 int pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_id);
 

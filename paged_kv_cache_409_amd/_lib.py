@@ -95,6 +95,7 @@ SIGNATURES = {
     "pkv_bm_add_sequence": (_c_int, [_c_p, _c_i64, _c_p, _c_int, _c_p, ctypes.POINTER(_c_int)]),
     "pkv_bm_append": (_c_int, [_c_p, _c_i64, _c_p, _c_int, _c_p, _c_p, _c_int, ctypes.POINTER(_c_int)]),
     "pkv_bm_append_batch": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_p, _c_p, _c_int, ctypes.POINTER(_c_int)]),
+    "pkv_bm_append_step": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_p, _c_p]),
     "pkv_bm_fork": (_c_int, [_c_p, _c_i64, _c_i64]),
     "pkv_bm_free": (_c_int, [_c_p, _c_i64]),
     "pkv_bm_block_tables": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, ctypes.c_int32, _c_p]),

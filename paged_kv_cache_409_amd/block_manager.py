@@ -82,6 +82,18 @@ class BlockManager:
             self._h, _ptr(ids), n, _ptr(t), _ptr(slots), _ptr(pairs), n, ctypes.byref(ncow)))
         return slots, pairs[:ncow.value]
 
+    def append_step(self, seq_ids, tokens=None):
+        """append_batch for decode_step's fused copy-on-write. Returns (slots int64 [n],
+        cow_src int32 [n]: each sequence's copy-on-write source, -1: none)."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = len(ids)
+        t = self._tokens(tokens, n)
+        slots = np.empty(n, dtype=np.int64)
+        cow_src = np.empty(max(n, 1), dtype=np.int32)
+        self._check("pkv_bm_append_step", self._lib.pkv_bm_append_step(
+            self._h, _ptr(ids), n, _ptr(t), _ptr(slots), _ptr(cow_src)))
+        return slots, cow_src[:n]
+
     def fork(self, parent_id: int, child_id: int) -> None:
         self._check("pkv_bm_fork", self._lib.pkv_bm_fork(self._h, parent_id, child_id))
 

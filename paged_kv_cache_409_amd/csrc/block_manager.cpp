@@ -10,6 +10,7 @@
 //   reused as a free block only when the free queue is empty;
 // * every call checks what it needs (sequence ids, blocks, output room) before it changes
 //   anything, so a failed call leaves the manager as it was.
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <deque>
@@ -312,6 +313,26 @@ int pkv_bm_append_batch(pkv_block_manager* bm, const int64_t* seq_ids, int n, co
     ncow += c;
   }
   if (num_cow) *num_cow = ncow;
+  return PKV_OK;
+}
+
+int pkv_bm_append_step(pkv_block_manager* bm, const int64_t* seq_ids, int n, const int32_t* tokens,
+                       int64_t* slots_out, int32_t* cow_src_out) {
+  if (!bm) return PKV_ERR_NULL;
+  if (n < 0) return PKV_ERR_SHAPE;
+  if (n > 0 && !cow_src_out) return PKV_ERR_NULL;
+  // At most one copy per sequence; the batch call checks everything before changing anything.
+  std::vector<int64_t> pairs(2 * (size_t)std::max(n, 1));
+  int ncow = 0;
+  const int st = pkv_bm_append_batch(bm, seq_ids, n, tokens, slots_out, pairs.data(), n, &ncow);
+  if (st != PKV_OK) return st;
+  // Each pair's fresh block holds the new token of exactly one sequence of the step.
+  std::unordered_map<int64_t, int64_t> src_of;   // fresh block -> its source
+  for (int k = 0; k < ncow; ++k) src_of[pairs[2 * k + 1]] = pairs[2 * k];
+  for (int i = 0; i < n; ++i) {
+    const auto it = src_of.find(slots_out[i] / bm->P);
+    cow_src_out[i] = it == src_of.end() ? -1 : (int32_t)it->second;
+  }
   return PKV_OK;
 }
 

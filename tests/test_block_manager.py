@@ -270,3 +270,34 @@ def test_a_batched_step_equals_single_appends():
         tight.add_sequence(5, 0)
         tight.append_batch([0, 1, 5])       # one copy and one new block, but one block free
     assert e.value.status == ERR_NO_BLOCKS and tight.num_free() == state
+
+
+def test_a_step_for_the_fused_copy_names_each_sequences_source():
+    # append_step makes the same appends as append_batch and reports, per sequence, the
+    # source of the copy whose fresh block takes its new token (-1: none), the cow_src of
+    # decode_step; a failing step changes nothing either.
+    def setup():
+        bm = BlockManager(12)
+        bm.add_sequence(0, 20)
+        for k in (1, 2, 3):
+            bm.fork(0, k)
+        bm.add_sequence(9, 16)
+        return bm
+    a, b = setup(), setup()
+    ids = [1, 2, 3, 0, 9]
+    slots, pairs = a.append_batch(ids)
+    slots2, cow_src = b.append_step(ids)
+    assert slots2.tolist() == slots.tolist() and cow_src.dtype == np.int32
+    expect = {int(dst): int(src) for src, dst in pairs.tolist()}
+    assert cow_src.tolist() == [expect.get(int(s) // 16, -1) for s in slots.tolist()]
+    assert cow_src.tolist()[:3] == [int(p[0]) for p in pairs.tolist()] and cow_src.tolist()[3:] == [-1, -1]
+    assert a.num_free() == b.num_free()
+    assert b.append_step([])[1].tolist() == []
+    tight = BlockManager(3)
+    tight.add_sequence(0, 20)
+    tight.fork(0, 1)
+    tight.add_sequence(5, 0)
+    state = tight.num_free()
+    with pytest.raises(PkvError) as e:
+        tight.append_step([0, 1, 5])
+    assert e.value.status == ERR_NO_BLOCKS and tight.num_free() == state

@@ -73,3 +73,51 @@ def test_beams_with_prefix_caching_through_the_kernels(kv_dtype):
                                            scale_kv, scale_kv)
     err = float(np.abs(out.float().cpu().numpy() - ref).max())
     assert err <= (3e-2 if kv_dtype == "fp8_e4m3" else 1e-2), err
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_beam_step_with_the_copies_fused_through_the_kernels(kv_dtype):
+    # The same kind of history, then one decode step of the manager (append_step) run as one
+    # fused launch: copy-on-write of the shared partial blocks (cow_src), the new tokens'
+    # write and attention. The oracle replays the copies as pairs, the write and the decode.
+    rng = np.random.default_rng(21)
+    P, Hkv, G, D, NB = 16, 2, 4, 128, 160
+    kv_t = torch.uint8 if kv_dtype == "fp8_e4m3" else torch.bfloat16
+    scale_kv = 1 / 64 if kv_dtype == "fp8_e4m3" else 1.0
+    bm = BlockManager(NB)
+    k_cache = torch.zeros((NB, Hkv, P, D), dtype=kv_t, device="cuda")
+    v_cache = torch.zeros_like(k_cache)
+    for r, n in enumerate((45, 70)):
+        slots, _ = bm.add_sequence(100 * r, n)
+        k = torch.randn((n, Hkv, D), device="cuda").to(torch.bfloat16)
+        v = torch.randn((n, Hkv, D), device="cuda").to(torch.bfloat16)
+        pkv.reshape_and_cache(k, v, torch.from_numpy(slots).cuda(), k_cache, v_cache, scale_kv, scale_kv)
+    seqs = []
+    for r in range(2):
+        for b in range(4):
+            bm.fork(100 * r, 100 * r + 1 + b)
+            seqs.append(100 * r + 1 + b)
+        bm.free(100 * r)
+    torch.cuda.synchronize()
+    hk, hv = torch_bits(k_cache), torch_bits(v_cache)
+    slots, cow_src = bm.append_step(seqs)
+    pairs = np.array([(int(c), int(s) // P) for c, s in zip(cow_src, slots) if c >= 0], dtype=np.int64)
+    assert len(pairs) == 6
+    tables, ctx = bm.block_tables(seqs, 8, pad_block=NB - 1)
+    q = torch.randn((len(seqs), Hkv * G, D), device="cuda").to(torch.bfloat16)
+    k_new = torch.randn((len(seqs), Hkv, D), device="cuda").to(torch.bfloat16)
+    v_new = torch.randn((len(seqs), Hkv, D), device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    say("block manager, fused copy-on-write step", kv_dtype)
+    pkv.decode_step(out, q, k_cache, v_cache, k_new, v_new, torch.from_numpy(slots).cuda(),
+                    torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda(), D ** -0.5, int(ctx.max()),
+                    scale_kv, scale_kv, cow_src=torch.from_numpy(cow_src).cuda())
+    torch.cuda.synchronize()
+    (hk,), (hv,) = cache_ops.copy_blocks([hk], [hv], pairs)
+    hk, hv = cache_ops.reshape_and_cache(torch_bits(k_new), torch_bits(v_new), slots, hk, hv, "bf16", kv_dtype,
+                                         scale_kv, scale_kv)
+    assert np.array_equal(torch_bits(k_cache), hk) and np.array_equal(torch_bits(v_cache), hv)
+    ref = attention.paged_decode_attention(torch_bits(q), hk, hv, tables, ctx, D ** -0.5, "bf16", kv_dtype,
+                                           scale_kv, scale_kv)
+    err = float(np.abs(out.float().cpu().numpy() - ref).max())
+    assert err <= (3e-2 if kv_dtype == "fp8_e4m3" else 1e-2), err
