@@ -1,6 +1,6 @@
 """Benchmark of one paged decode step (or one prefill chunk) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 50] [--config llama2_70b_gqa]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 500] [--config llama2_70b_gqa]
     python bench.py --config prefill_70b_gqa      (a prefill-chunk step, see prefill_bench)
     python bench.py --config swap_70b             (blocks out to pinned host memory and back, see swap_bench)
     python bench.py --config block_manager        (host bookkeeping of decode steps, see block_manager_bench)
@@ -78,11 +78,12 @@ def load_traffic(config_name: str, kind: str = "decode", sources=DECODE_SOURCES)
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # A step is about 0.1 ms: 50 warm-up steps give the device several milliseconds of
-    # this work before timing (with 10, the first timed steps of the beam workload ran
-    # about 10% slower), and 200 timed steps take about 25 ms.
+    # A step is about 0.1 ms. The first few hundred steps of a run are slower than the
+    # rest: after 10 warm-up steps the beam workload's timed steps ran about 10% slower,
+    # after 50 about 3% (the 70B batch about 0.5%), after 400 no slower than later ones. 500
+    # warm-up steps take about 55 ms, and 200 timed steps about 25 ms.
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--config", default="llama2_70b_gqa")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
