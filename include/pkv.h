@@ -62,8 +62,9 @@
 extern "C" {
 #endif
 
-/* 2: pkv_decode_step and pkv_decode_step_no_alloc take cow_src. */
-#define PKV_API_VERSION 2
+/* 2: pkv_decode_step and pkv_decode_step_no_alloc take cow_src.
+ * 3: pkv_validate_inputs and pkv_validate_inputs_host take cow_src (pkv_validate.h). */
+#define PKV_API_VERSION 3
 
 /* Element types. */
 typedef enum pkv_dtype {

@@ -20,7 +20,11 @@
  *   written by one pkv_copy_blocks call are distinct and are not read by the same call;
  * - pkv_decode_step writes sequence s's new token into the slot of its last position,
  *   context_lens[s] - 1, in a block that no other sequence of the batch reads (a shared
- *   block is copied first).
+ *   block is copied first);
+ * - with cow_src, pkv_decode_step first makes that block a copy of block cow_src[s] (the
+ *   same section's copy-on-write, done inside the step), so the source is a block of the
+ *   pool, the sequence has a last block to copy into, and no other sequence reads that
+ *   block in the step, neither through its table nor as its own copy's source.
  *
  * Both calls are synchronous and meant for debugging, not for the hot path. They allocate
  * host memory only. The result names the first failed check in the order of pkv_check.
@@ -47,7 +51,14 @@ typedef enum pkv_check {
                                        index = s, value = the other sequence */
   PKV_CHECK_PAIR_RANGE = 7,         /* a copy pair's src or dst is outside [0, num_blocks); index = pair */
   PKV_CHECK_PAIR_DUPLICATE_DST = 8, /* a dst already written by an earlier pair; index = the later pair */
-  PKV_CHECK_PAIR_DST_IS_SRC = 9     /* a dst that is also the src of another pair; index = the pair writing it */
+  PKV_CHECK_PAIR_DST_IS_SRC = 9,    /* a dst that is also the src of another pair; index = the pair writing it */
+  PKV_CHECK_COW_RANGE = 10,         /* decode step: cow_src[s] < -1 or >= num_blocks; index = s */
+  PKV_CHECK_COW_NO_CONTEXT = 11,    /* decode step: cow_src[s] >= 0 for a sequence with no context (no block
+                                       to copy into); index = s, value = cow_src[s] */
+  PKV_CHECK_COW_SHARED_DST = 12,    /* decode step: the block that sequence s's copy writes holds context of
+                                       another sequence; index = s, value = the other sequence */
+  PKV_CHECK_COW_DST_IS_SRC = 13     /* decode step: the block that sequence s's copy writes is the copy
+                                       source of another sequence; index = s, value = the other sequence */
 } pkv_check;
 
 typedef struct pkv_validation {
@@ -65,6 +76,8 @@ typedef struct pkv_validation {
  *   slot_mapping   [num_tokens] int64 (negative = no write), or NULL
  *   decode_step    nonzero: slot_mapping is pkv_decode_step's (num_tokens == num_seqs,
  *                  token s belongs to sequence s; needs block_tables and context_lens)
+ *   cow_src        [num_seqs] int32 as for pkv_decode_step (-1: no copy), or NULL; needs
+ *                  decode_step. A source equal to its destination is a no-op and passes.
  *   src_dst_pairs  [num_pairs, 2] int64 (src, dst) as for pkv_copy_blocks, or NULL
  *   block_size     16, 32 or 64
  *   result         written with the first failed check, or PKV_CHECK_OK
@@ -72,23 +85,27 @@ typedef struct pkv_validation {
  * Returns PKV_OK when the checks ran (the verdict is in *result), a negative pkv_status
  * when the arguments themselves are inconsistent (NULL result, negative sizes, one of
  * block_tables / context_lens without the other, decode_step without them or with
- * num_tokens != num_seqs).
+ * num_tokens != num_seqs: PKV_ERR_NULL or PKV_ERR_SHAPE; cow_src without decode_step:
+ * PKV_ERR_SHAPE).
  */
 int pkv_validate_inputs_host(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                              int max_blocks_per_seq, int block_size, int64_t num_blocks,
                              const int64_t* slot_mapping, int num_tokens, int decode_step,
-                             const int64_t* src_dst_pairs, int num_pairs, pkv_validation* result);
+                             const int32_t* cow_src, const int64_t* src_dst_pairs, int num_pairs,
+                             pkv_validation* result);
 
 /*
  * The same checks on device buffers: copies them to host memory on `stream` (a
  * hipStream_t as void*, NULL = the default stream), waits for the copies, then checks as
  * pkv_validate_inputs_host does. Device pointers: block_tables, context_lens,
- * slot_mapping, src_dst_pairs; result is a host pointer. PKV_ERR_HIP when a copy fails.
+ * slot_mapping, cow_src, src_dst_pairs; result is a host pointer. PKV_ERR_HIP when a copy
+ * fails.
  */
 int pkv_validate_inputs(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                         int max_blocks_per_seq, int block_size, int64_t num_blocks,
                         const int64_t* slot_mapping, int num_tokens, int decode_step,
-                        const int64_t* src_dst_pairs, int num_pairs, void* stream, pkv_validation* result);
+                        const int32_t* cow_src, const int64_t* src_dst_pairs, int num_pairs, void* stream,
+                        pkv_validation* result);
 
 #ifdef __cplusplus
 }

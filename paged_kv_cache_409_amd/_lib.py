@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 1, 2, 3
 PKV_NO_ALLOC_SCRATCH_BYTES = 32 << 20     # include/pkv.h
-API_VERSION = 2                           # PKV_API_VERSION, include/pkv.h
+API_VERSION = 3                           # PKV_API_VERSION, include/pkv.h
 
 _c_int, _c_i64, _c_f, _c_p, _c_sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -83,11 +83,11 @@ SIGNATURES = {
     # include/pkv_validate.h (debug checks of index-buffer values)
     "pkv_validate_inputs_host": (_c_int, [
         _c_p, _c_p, _c_int, _c_int, _c_int, _c_i64,    # block_tables context_lens num_seqs max_blocks block_size num_blocks
-        _c_p, _c_int, _c_int,                          # slot_mapping num_tokens decode_step
+        _c_p, _c_int, _c_int, _c_p,                    # slot_mapping num_tokens decode_step cow_src
         _c_p, _c_int, ctypes.POINTER(Validation)]),    # src_dst_pairs num_pairs result
     "pkv_validate_inputs": (_c_int, [
         _c_p, _c_p, _c_int, _c_int, _c_int, _c_i64,
-        _c_p, _c_int, _c_int,
+        _c_p, _c_int, _c_int, _c_p,
         _c_p, _c_int, _c_p, ctypes.POINTER(Validation)]),   # ... stream result
     # include/pkv_block_manager.h (host-side bookkeeping)
     "pkv_bm_create": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_p)]),

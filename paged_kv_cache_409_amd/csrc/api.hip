@@ -569,14 +569,15 @@ int pkv_swap_blocks(const void* const* src_k_caches, const void* const* src_v_ca
 int pkv_validate_inputs(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                         int max_blocks_per_seq, int block_size, int64_t num_blocks,
                         const int64_t* slot_mapping, int num_tokens, int decode_step,
-                        const int64_t* src_dst_pairs, int num_pairs, void* stream, pkv_validation* result) {
+                        const int32_t* cow_src, const int64_t* src_dst_pairs, int num_pairs, void* stream,
+                        pkv_validation* result) {
   if (!result) return PKV_ERR_NULL;
   if (num_seqs < 0 || num_tokens < 0 || num_pairs < 0 || max_blocks_per_seq < 0) return PKV_ERR_SHAPE;
   if ((block_tables != nullptr) != (context_lens != nullptr)) return PKV_ERR_NULL;
   if (num_pairs > 0 && !src_dst_pairs) return PKV_ERR_NULL;
   // Host copies of the buffers, then the host checks (which repeat the argument checks).
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  std::vector<int32_t> bt, cl;
+  std::vector<int32_t> bt, cl, cs;
   std::vector<int64_t> sm, pr;
   hipError_t e = hipSuccess;
   if (block_tables) {
@@ -591,6 +592,10 @@ int pkv_validate_inputs(const int32_t* block_tables, const int32_t* context_lens
     sm.resize((size_t)num_tokens);
     e = hipMemcpyAsync(sm.data(), slot_mapping, sm.size() * sizeof(int64_t), hipMemcpyDeviceToHost, s);
   }
+  if (e == hipSuccess && cow_src && num_seqs > 0) {
+    cs.resize((size_t)num_seqs);
+    e = hipMemcpyAsync(cs.data(), cow_src, cs.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  }
   if (e == hipSuccess && num_pairs > 0) {
     pr.resize((size_t)num_pairs * 2);
     e = hipMemcpyAsync(pr.data(), src_dst_pairs, pr.size() * sizeof(int64_t), hipMemcpyDeviceToHost, s);
@@ -604,7 +609,8 @@ int pkv_validate_inputs(const int32_t* block_tables, const int32_t* context_lens
                                   context_lens ? (cl.empty() ? &kNoInt : cl.data()) : nullptr, num_seqs,
                                   max_blocks_per_seq, block_size, num_blocks,
                                   slot_mapping ? (sm.empty() ? &kNoLong : sm.data()) : nullptr, num_tokens,
-                                  decode_step, num_pairs > 0 ? pr.data() : nullptr, num_pairs, result);
+                                  decode_step, cow_src ? (cs.empty() ? &kNoInt : cs.data()) : nullptr,
+                                  num_pairs > 0 ? pr.data() : nullptr, num_pairs, result);
 }
 
 }  // extern "C"

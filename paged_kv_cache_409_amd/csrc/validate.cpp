@@ -21,7 +21,8 @@ void fail(pkv_validation* r, int check, int64_t index, int64_t value) {
 extern "C" int pkv_validate_inputs_host(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                                         int max_blocks_per_seq, int block_size, int64_t num_blocks,
                                         const int64_t* slot_mapping, int num_tokens, int decode_step,
-                                        const int64_t* src_dst_pairs, int num_pairs, pkv_validation* result) {
+                                        const int32_t* cow_src, const int64_t* src_dst_pairs, int num_pairs,
+                                        pkv_validation* result) {
   if (!result) return PKV_ERR_NULL;
   if (num_seqs < 0 || num_tokens < 0 || num_pairs < 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
   if (block_size != 16 && block_size != 32 && block_size != 64) return PKV_ERR_UNSUPPORTED;
@@ -30,6 +31,7 @@ extern "C" int pkv_validate_inputs_host(const int32_t* block_tables, const int32
   if (tables && max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
   if (decode_step && (!tables || !slot_mapping)) return PKV_ERR_NULL;
   if (decode_step && num_tokens != num_seqs) return PKV_ERR_SHAPE;
+  if (cow_src && !decode_step) return PKV_ERR_SHAPE;
   fail(result, PKV_CHECK_OK, -1, 0);
 
   const int64_t P = block_size;
@@ -96,6 +98,46 @@ extern "C" int pkv_validate_inputs_host(const int32_t* block_tables, const int32
             return PKV_OK;
           }
         }
+      }
+    }
+  }
+
+  if (cow_src) {
+    // The step's copies: each sequence's last block (the destination) becomes a copy of
+    // cow_src[s] before its new token lands there.
+    for (int s = 0; s < num_seqs; ++s) {
+      const int64_t b = cow_src[s];
+      if (b < -1 || b >= num_blocks) {
+        fail(result, PKV_CHECK_COW_RANGE, s, b);
+        return PKV_OK;
+      }
+      if (b >= 0 && context_lens[s] == 0) {
+        fail(result, PKV_CHECK_COW_NO_CONTEXT, s, b);
+        return PKV_OK;
+      }
+    }
+    std::unordered_map<int64_t, int> dst_of;   // destination block -> copying sequence
+    for (int s = 0; s < num_seqs; ++s) {
+      if (cow_src[s] < 0) continue;
+      const int64_t dst = block_tables[(int64_t)s * max_blocks_per_seq + (context_lens[s] - 1) / P];
+      if (dst != cow_src[s]) dst_of.emplace(dst, s);   // a copy onto itself is a no-op
+    }
+    for (int t = 0; t < num_seqs; ++t) {
+      const int64_t used = (context_lens[t] + P - 1) / P;
+      for (int64_t i = 0; i < used; ++i) {
+        const auto it = dst_of.find(block_tables[(int64_t)t * max_blocks_per_seq + i]);
+        if (it != dst_of.end() && it->second != t) {
+          fail(result, PKV_CHECK_COW_SHARED_DST, it->second, t);
+          return PKV_OK;
+        }
+      }
+    }
+    for (int t = 0; t < num_seqs; ++t) {
+      if (cow_src[t] < 0) continue;
+      const auto it = dst_of.find(cow_src[t]);
+      if (it != dst_of.end() && it->second != t) {
+        fail(result, PKV_CHECK_COW_DST_IS_SRC, it->second, t);
+        return PKV_OK;
       }
     }
   }

@@ -285,11 +285,13 @@ def swap_blocks(src_k_caches, src_v_caches, dst_k_caches, dst_v_caches, src_dst_
 
 
 CHECKS = {0: "ok", 1: "context_len", 2: "block_id", 3: "slot_range", 4: "slot_duplicate", 5: "slot_not_last",
-          6: "slot_shared_block", 7: "pair_range", 8: "pair_duplicate_dst", 9: "pair_dst_is_src"}
+          6: "slot_shared_block", 7: "pair_range", 8: "pair_duplicate_dst", 9: "pair_dst_is_src",
+          10: "cow_range", 11: "cow_no_context", 12: "cow_shared_dst", 13: "cow_dst_is_src"}
 
 
 def validate_inputs(num_blocks: int, block_tables=None, context_lens=None, slot_mapping=None, src_dst_pairs=None,
-                    block_size: int = 16, decode_step: bool = False, stream=None) -> tuple[str, int, int]:
+                    block_size: int = 16, decode_step: bool = False, stream=None,
+                    cow_src=None) -> tuple[str, int, int]:
     """Debug check of the values in the index buffers (see include/pkv_validate.h).
 
     Returns (check, index, value): ("ok", -1, 0), or the name of the first failed check with
@@ -297,15 +299,18 @@ def validate_inputs(num_blocks: int, block_tables=None, context_lens=None, slot_
     pkv_validate_inputs (copied to the host on `stream`), CPU tensors through
     pkv_validate_inputs_host; all given tensors must be on the same side.
     """
-    given = [t for t in (block_tables, context_lens, slot_mapping, src_dst_pairs) if t is not None]
+    given = [t for t in (block_tables, context_lens, slot_mapping, src_dst_pairs, cow_src) if t is not None]
     on_gpu = {bool(t.is_cuda) for t in given}
     if len(on_gpu) > 1:
         raise ValueError("index tensors must all be on the GPU or all on the CPU")
     for t, dt, name in ((block_tables, torch.int32, "block_tables"), (context_lens, torch.int32, "context_lens"),
-                        (slot_mapping, torch.int64, "slot_mapping"), (src_dst_pairs, torch.int64, "src_dst_pairs")):
+                        (slot_mapping, torch.int64, "slot_mapping"), (src_dst_pairs, torch.int64, "src_dst_pairs"),
+                        (cow_src, torch.int32, "cow_src")):
         if t is not None and (t.dtype != dt or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous {dt} tensor")
     S = context_lens.shape[0] if context_lens is not None else 0
+    if cow_src is not None and tuple(cow_src.shape) != (S,):
+        raise ValueError("cow_src must be int32 [num_seqs]")
     maxb = block_tables.shape[1] if block_tables is not None and block_tables.dim() == 2 else 0
     T = slot_mapping.shape[0] if slot_mapping is not None else 0
     n_pairs = src_dst_pairs.shape[0] if src_dst_pairs is not None else 0
@@ -316,7 +321,7 @@ def validate_inputs(num_blocks: int, block_tables=None, context_lens=None, slot_
     res = _lib.Validation()
     lib = _lib.load()
     common = (ptr(block_tables), ptr(context_lens), S, maxb, block_size, num_blocks, ptr(slot_mapping), T,
-              1 if decode_step else 0, ptr(src_dst_pairs), n_pairs)
+              1 if decode_step else 0, ptr(cow_src), ptr(src_dst_pairs), n_pairs)
     if on_gpu == {True}:
         st = lib.pkv_validate_inputs(*common, _stream(stream), ctypes.byref(res))
         _check("pkv_validate_inputs", st)

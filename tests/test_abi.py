@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    assert lib.pkv_api_version() == _lib.API_VERSION == 2
+    assert lib.pkv_api_version() == _lib.API_VERSION == 3
     for code in range(0, -8, -1):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(-99) == b"unknown status"

@@ -21,11 +21,15 @@ def test_device_buffers_give_the_host_verdicts():
     sm[6] = sm[1]
     pairs = b.copy_pairs.clone()
     pairs[1, 1] = pairs[0, 1]
-    cases = [dict(), dict(context_lens=ctx), dict(slot_mapping=sm), dict(src_dst_pairs=pairs),
-             dict(slot_mapping=None, decode_step=False), dict(block_tables=None, context_lens=None, decode_step=False)]
+    cow = b.cow_src.clone()
+    s, t = [i for i in range(cfg.num_seqs) if int(cow[i]) >= 0][:2]
+    cow[t] = b.block_tables[s, (int(b.context_lens[s]) - 1) // 16]
+    cases = [dict(), dict(context_lens=ctx), dict(slot_mapping=sm), dict(src_dst_pairs=pairs), dict(cow_src=cow),
+             dict(cow_src=None), dict(slot_mapping=None, decode_step=False, cow_src=None),
+             dict(block_tables=None, context_lens=None, decode_step=False, cow_src=None)]
     for over in cases:
         args = dict(block_tables=b.block_tables, context_lens=b.context_lens, slot_mapping=b.slot_mapping,
-                    src_dst_pairs=b.copy_pairs, decode_step=True)
+                    src_dst_pairs=b.copy_pairs, decode_step=True, cow_src=b.cow_src)
         args.update(over)
         host = pkv.validate_inputs(cfg.num_blocks, **args)
         dev = pkv.validate_inputs(cfg.num_blocks, **{k: (v.cuda() if isinstance(v, torch.Tensor) else v)
@@ -33,4 +37,4 @@ def test_device_buffers_give_the_host_verdicts():
         say("validate", sorted(over), host)
         assert dev == host
     assert pkv.validate_inputs(cfg.num_blocks, b.block_tables.cuda(), b.context_lens.cuda(), b.slot_mapping.cuda(),
-                               b.copy_pairs.cuda(), decode_step=True) == ("ok", -1, 0)
+                               b.copy_pairs.cuda(), decode_step=True, cow_src=b.cow_src.cuda()) == ("ok", -1, 0)
