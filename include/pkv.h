@@ -180,7 +180,10 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
  *                  token is written into it: the results are those of
  *                  pkv_copy_blocks(pairs (cow_src[s], that block)) followed by the two calls
  *                  above, bit for bit. -1 (or an id outside the pool) copies nothing. No
- *                  other sequence may read the destination block in the same step.
+ *                  other sequence may read the destination block in the same step, and
+ *                  another sequence's new token may land in the source only in the row of
+ *                  s's own new token (the one row the copy does not take; beams that share
+ *                  a partial block hold the same tokens in it, so theirs share that row).
  *   k_cache/v_cache written (copies, new tokens converted as pkv_reshape_and_cache does, fp8
  *                  with k_scale / v_scale) and read
  * Every other argument is as for pkv_paged_attention_decode, whose checks also apply.

@@ -24,7 +24,9 @@
  * - with cow_src, pkv_decode_step first makes that block a copy of block cow_src[s] (the
  *   same section's copy-on-write, done inside the step), so the source is a block of the
  *   pool, the sequence has a last block to copy into, and no other sequence reads that
- *   block in the step, neither through its table nor as its own copy's source.
+ *   block in the step, neither through its table nor as its own copy's source; the copy
+ *   reads its source in the same launch, so another sequence's new token may land there
+ *   only in the row of the copying sequence's own new token, which the copy does not take.
  *
  * Both calls are synchronous and meant for debugging, not for the hot path. They allocate
  * host memory only. The result names the first failed check in the order of pkv_check.
@@ -57,8 +59,11 @@ typedef enum pkv_check {
                                        to copy into); index = s, value = cow_src[s] */
   PKV_CHECK_COW_SHARED_DST = 12,    /* decode step: the block that sequence s's copy writes holds context of
                                        another sequence; index = s, value = the other sequence */
-  PKV_CHECK_COW_DST_IS_SRC = 13     /* decode step: the block that sequence s's copy writes is the copy
+  PKV_CHECK_COW_DST_IS_SRC = 13,    /* decode step: the block that sequence s's copy writes is the copy
                                        source of another sequence; index = s, value = the other sequence */
+  PKV_CHECK_COW_SRC_WRITTEN = 14    /* decode step: another sequence's new token lands in sequence s's copy
+                                       source at a row the copy takes (any row but that of s's own new
+                                       token); index = s, value = the other sequence */
 } pkv_check;
 
 typedef struct pkv_validation {

@@ -140,6 +140,27 @@ extern "C" int pkv_validate_inputs_host(const int32_t* block_tables, const int32
         return PKV_OK;
       }
     }
+    // A copy takes every row of its source but its own new token's; another sequence's new
+    // token may land in the source only in that row (beams that shared the block hold the
+    // same number of tokens in it, so their new tokens share the row).
+    std::unordered_map<int64_t, std::vector<int>> copies_from;   // source block -> copying sequences
+    for (const auto& [dst, s] : dst_of) copies_from[cow_src[s]].push_back(s);
+    for (int t = 0; t < num_seqs; ++t) {
+      const int64_t slot = slot_mapping[t];
+      if (slot < 0) continue;
+      const auto it = copies_from.find(slot / P);
+      if (it == copies_from.end()) continue;
+      for (const int s : it->second) {
+        if (s == t) continue;
+        const int64_t dst = block_tables[(int64_t)s * max_blocks_per_seq + (context_lens[s] - 1) / P];
+        const int64_t own = slot_mapping[s];
+        const int64_t skip = (own >= 0 && own / P == dst) ? own % P : -1;
+        if (slot % P != skip) {
+          fail(result, PKV_CHECK_COW_SRC_WRITTEN, s, t);
+          return PKV_OK;
+        }
+      }
+    }
   }
 
   if (num_pairs > 0) {

@@ -286,7 +286,7 @@ def swap_blocks(src_k_caches, src_v_caches, dst_k_caches, dst_v_caches, src_dst_
 
 CHECKS = {0: "ok", 1: "context_len", 2: "block_id", 3: "slot_range", 4: "slot_duplicate", 5: "slot_not_last",
           6: "slot_shared_block", 7: "pair_range", 8: "pair_duplicate_dst", 9: "pair_dst_is_src",
-          10: "cow_range", 11: "cow_no_context", 12: "cow_shared_dst", 13: "cow_dst_is_src"}
+          10: "cow_range", 11: "cow_no_context", 12: "cow_shared_dst", 13: "cow_dst_is_src", 14: "cow_src_written"}
 
 
 def validate_inputs(num_blocks: int, block_tables=None, context_lens=None, slot_mapping=None, src_dst_pairs=None,
