@@ -121,7 +121,7 @@ def gpu_bench(args, pool) -> int:
     import torch
 
     import paged_kv_cache_409_amd as pkv
-    from workloads import BLOCK_SIZE_CONFIGS, CONFIGS, PREFILL_CONFIGS, SWAP_CONFIGS, make_batch
+    from workloads import BLOCK_SIZE_CONFIGS, CONFIGS, PREFILL_CONFIGS, SHARD_CONFIGS, SWAP_CONFIGS, make_batch
     from workloads.gen import kv_bytes_logical, kv_bytes_unique
 
     dev = torch.device("cuda:0")
@@ -134,7 +134,7 @@ def gpu_bench(args, pool) -> int:
         return swap_bench(args, SWAP_CONFIGS[args.config], dev)
     if args.config == "cache_ops":
         return cache_ops_bench(args, dev)
-    cfg = {**CONFIGS, **BLOCK_SIZE_CONFIGS}[args.config]
+    cfg = {**CONFIGS, **BLOCK_SIZE_CONFIGS, **SHARD_CONFIGS}[args.config]
     batches = [make_batch(cfg, dev, replica=r) for r in range(args.replicas)]
     lay = batches[0].layout
     # Replicas draw their own context lengths: each step counts the bytes of its own batch.

@@ -8,7 +8,7 @@ from tests._gpu import (HostBatch, clone_batch, device_batch, gpu_fused_step, gp
                         oracle_caches_after_step, oracle_decode, say, tol)
 from tests._paged import torch_bits
 from tests.test_gpu_decode import small_cfg
-from workloads import CONFIGS, WorkloadConfig, make_batch
+from workloads import ALL_CONFIGS, WorkloadConfig, make_batch
 
 pytestmark = pytest.mark.gpu
 
@@ -69,11 +69,11 @@ def test_fused_step_zero_length_rows_and_skipped_slots(G):
     assert (out[2] == 0).all()
 
 
-@pytest.mark.parametrize("name", ["llama2_7b", "llama2_70b_gqa", "long_cot", "beam_cow"])
+@pytest.mark.parametrize("name", ["llama2_7b", "llama2_70b_gqa", "long_cot", "beam_cow", "llama2_70b_gqa_tp8"])
 def test_full_size_fused_step(name):
     # The launch the benchmark times, on one of its replicas: caches bit for bit and every
     # sequence, head and column of the output against the oracle.
-    cfg = CONFIGS[name]
+    cfg = ALL_CONFIGS[name]
     say(name, "generate")
     b = make_batch(cfg, "cuda", replica=1)
     say(name, "fused step")

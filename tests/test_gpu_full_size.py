@@ -8,14 +8,14 @@ import torch
 
 from tests._gpu import HostBatch, gpu_step, max_err, oracle_caches_after_step, oracle_decode, say, tol
 from tests._paged import torch_bits
-from workloads import CONFIGS, make_batch
+from workloads import ALL_CONFIGS, make_batch
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["tiny", "llama2_7b", "llama2_70b_gqa", "long_cot", "beam_cow"])
+@pytest.mark.parametrize("name", ["tiny", "llama2_7b", "llama2_70b_gqa", "long_cot", "beam_cow", "llama2_70b_gqa_tp8"])
 def test_full_size_step_matches_oracle(name):
-    cfg = CONFIGS[name]
+    cfg = ALL_CONFIGS[name]
     say(name, "generate")
     b = make_batch(cfg, "cuda", replica=0)
     h = HostBatch(b)

@@ -108,4 +108,12 @@ LLAMA2_70B_GQA_P32 = replace(LLAMA2_70B_GQA, name="llama2_70b_gqa_p32", block_si
 LLAMA2_70B_GQA_P64 = replace(LLAMA2_70B_GQA, name="llama2_70b_gqa_p64", block_size=64, num_blocks=4096,
                              description="Llama-2-70B GQA layer with 64-token blocks (else as llama2_70b_gqa)")
 BLOCK_SIZE_CONFIGS = {c.name: c for c in (LLAMA2_70B_GQA_P32, LLAMA2_70B_GQA_P64)}
-ALL_CONFIGS = {**CONFIGS, **PREFILL_CONFIGS, **BLOCK_SIZE_CONFIGS}
+
+# One GPU's share of the Llama-2-70B GQA decode layer under 8-way tensor parallelism
+# ("vLLM 推理优化技术深度调研报告", 维度一.6): the kv heads split over the GPUs, so each holds
+# one kv head (and its 8 query heads) of every block, for the same 256 sequences and contexts.
+LLAMA2_70B_GQA_TP8 = replace(LLAMA2_70B_GQA, name="llama2_70b_gqa_tp8", num_q_heads=8, num_kv_heads=1,
+                             description="one GPU's share of the Llama-2-70B GQA layer at 8-way tensor parallelism: "
+                                         "batch 256, 8 q / 1 kv head, D 128, bf16, ctx U[512,768]")
+SHARD_CONFIGS = {c.name: c for c in (LLAMA2_70B_GQA_TP8,)}
+ALL_CONFIGS = {**CONFIGS, **PREFILL_CONFIGS, **BLOCK_SIZE_CONFIGS, **SHARD_CONFIGS}
