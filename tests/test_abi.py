@@ -184,3 +184,58 @@ def test_gather_probe_argument_errors():
     assert gp(None, p, p, p, 4, 8, 128, 16, 64, 4, 64, 2, p, None) == -1
     assert gp(p + 8, p, p, p, 4, 8, 128, 16, 64, 4, 64, 2, p, None) == -6     # cache alignment
     assert gp(p, p, p, p, 4, 8, 128, 16, 64, 4, 64, 2, p + 2, None) == -6     # sink alignment
+
+
+C_PROGRAM = r"""
+#include <stdint.h>
+#include <stdio.h>
+#include "pkv.h"
+#include "pkv_block_manager.h"
+#include "pkv_validate.h"
+
+int main(void) {
+  if (pkv_api_version() != PKV_API_VERSION) return 1;
+  if (pkv_status_string(PKV_ERR_SHAPE)[0] == 0) return 2;
+  /* Host-only calls: a prompt of 20 tokens, two beams, one decode step's appends. */
+  pkv_block_manager* bm = NULL;
+  if (pkv_bm_create(8, 0, 16, 0, &bm) != PKV_OK) return 3;
+  int64_t slots[20];
+  if (pkv_bm_add_sequence(bm, 0, NULL, 20, slots, NULL) != PKV_OK) return 4;
+  if (pkv_bm_fork(bm, 0, 1) != PKV_OK) return 5;
+  int64_t ids[2] = {0, 1}, step_slots[2];
+  int32_t cow[2];
+  if (pkv_bm_append_step(bm, ids, 2, NULL, step_slots, cow) != PKV_OK) return 6;
+  int32_t tables[2 * 4], ctx[2];
+  if (pkv_bm_block_tables(bm, ids, 2, tables, 4, -1, ctx) != PKV_OK) return 7;
+  pkv_validation v;
+  if (pkv_validate_inputs_host(tables, ctx, 2, 4, 16, 8, step_slots, 2, 1, cow, NULL, 0, &v) != PKV_OK) return 8;
+  printf("%d %d %d %d\n", (int)ctx[0], (int)ctx[1], (int)(cow[0] >= 0) + (int)(cow[1] >= 0), (int)v.check);
+  pkv_bm_destroy(bm);
+  return v.check == PKV_CHECK_OK ? 0 : 9;
+}
+"""
+
+
+def test_headers_are_c99_and_a_c_program_links(tmp_path):
+    # The ABI is plain C: each header compiles on its own as C99 (pedantic, warnings as
+    # errors), and a C program using all three links against the library and runs its
+    # host-only calls (no GPU needed).
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-x", "c",
+                            os.path.join(inc, h)], check=True)
+    src = tmp_path / "abi_use.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi_use"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc, str(src), "-L", libdir,
+                    "-lpkv", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.split() == ["21", "21", "1", "0"]
