@@ -352,7 +352,10 @@ int pkv_swap_blocks(const void* const* src_k_caches, const void* const* src_v_ca
  * that hold tokens 0 .. context_lens[s] - 1 (whole tiles), found through block_tables as
  * pkv_paged_attention_decode finds them, with the decode kernels' loads. It computes
  * nothing but the XOR of every 32-bit word it reads, which it XORs into sink[s *
- * num_kv_heads + g]; its rate is the ceiling of this access pattern on the device.
+ * num_kv_heads + g]; its rate is the ceiling of this access pattern on the device. Each
+ * wavefront reads a run of up to 32 tiles of one (sequence, kv head); runs are shortened
+ * (to 16, 8 or 4 tiles) when a small batch would otherwise give the device fewer than
+ * 4096 wavefronts.
  *
  *   k_cache, v_cache, block_tables, context_lens, num_seqs, num_kv_heads, head_dim,
  *   block_size, num_blocks, max_blocks_per_seq, max_context_len, kv_dtype

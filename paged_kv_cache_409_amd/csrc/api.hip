@@ -493,7 +493,11 @@ int pkv_gather_probe(const void* k_cache, const void* v_cache, const int32_t* bl
   if ((num_blocks << shift) > 0x7fffffffLL || ((int64_t)max_blocks_per_seq << shift) > 0x7fffffffLL / 16)
     return PKV_ERR_SHAPE;
   const long long tiles = ((long long)max_context_len + 15) / 16;
-  const long long chunks = (tiles + pkv::kProbeChunk - 1) / pkv::kProbeChunk;
+  int chunk = pkv::kProbeChunkMax;
+  while (chunk > pkv::kProbeChunkMin &&
+         (long long)num_seqs * num_kv_heads * ((tiles + chunk - 1) / chunk) < pkv::kProbeMinWaves)
+    chunk /= 2;
+  const long long chunks = (tiles + chunk - 1) / chunk;
   if ((long long)num_seqs * num_kv_heads * chunks > (1LL << 31) - 8) return PKV_ERR_SHAPE;
   if (num_seqs == 0 || chunks == 0) return PKV_OK;
   if (!k_cache || !v_cache || !block_tables || !context_lens || !sink) return PKV_ERR_NULL;
@@ -510,6 +514,7 @@ int pkv_gather_probe(const void* k_cache, const void* v_cache, const int32_t* bl
   a.num_kv_heads = num_kv_heads;
   a.max_blocks = max_blocks_per_seq;
   a.block_shift = shift;
+  a.chunk = chunk;
   a.num_chunks = (int)chunks;
   const int tile_bytes = 16 * head_dim * (kv_dtype == PKV_FP8_E4M3 ? 1 : 2);
   return hip_status(pkv::launch_gather_probe(a, tile_bytes, reinterpret_cast<hipStream_t>(stream)));

@@ -8,8 +8,8 @@
 // loads, streaming cache policy, whole rows per instruction) and does nothing with them
 // but an XOR, so that its rate is the ceiling of the pattern on the device it runs on;
 // the decode rate divided by it says how much of the achievable the decode kernels reach.
-// Each wavefront takes up to kProbeChunk tiles of one (sequence, kv head), so that short
-// and long contexts alike give the device thousands of wavefronts.
+// Each wavefront takes up to `chunk` tiles of one (sequence, kv head), so that short and
+// long contexts alike give the device thousands of wavefronts.
 #include "gather_probe.h"
 
 namespace pkv {
@@ -21,7 +21,7 @@ template <int TB>   // bytes of one kv head's 16-token tile
 __global__ __launch_bounds__(kWave * kProbeWaves) void gather_probe_kernel(const ProbeArgs a) {
   constexpr int L = TB / (16 * kWave);   // 16-byte loads per lane per tile, K or V
   static_assert(L >= 1 && TB % (16 * kWave) == 0, "whole rows per load instruction");
-  static_assert(kProbeChunk <= kWave, "one tile name per lane");
+  static_assert(kProbeChunkMax <= kWave, "one tile name per lane");
   const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   // Items (chunk, sequence, kv head), the kv head fastest, as the decode kernels order theirs.
   const long long item = (long long)blockIdx.x * kProbeWaves + w;
@@ -31,8 +31,8 @@ __global__ __launch_bounds__(kWave * kProbeWaves) void gather_probe_kernel(const
   const int s = (int)(rest % a.num_seqs), c = (int)(rest / a.num_seqs);
   const int shift = a.block_shift;
   const int ctx = min(max(a.context_lens[s], 0), (a.max_blocks * kBlock) << shift);
-  const int t0 = c * kProbeChunk;
-  const int cn = min(kProbeChunk, (ctx + kBlock - 1) / kBlock - t0);   // tiles of this wavefront
+  const int t0 = c * a.chunk;
+  const int cn = min(a.chunk, (ctx + kBlock - 1) / kBlock - t0);   // tiles of this wavefront
   if (cn <= 0) return;
   const int64_t head_stride = (int64_t)TB << shift;
   const int64_t block_stride = (int64_t)a.num_kv_heads * head_stride;
