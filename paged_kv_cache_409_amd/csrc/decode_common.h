@@ -110,10 +110,13 @@ __device__ __forceinline__ Item decode_item(int j, const DecodeArgs& a) {
   return it;
 }
 
-// Grid of a decode launch: num_items padded for item_of_workgroup.
+// Grid of a decode launch: item_of_workgroup reaches items in whole blocks of 8 * xcd_run
+// workgroups, so the grid covers num_items in such blocks (then rounds up to 32, which
+// only adds ids past num_items).
 inline int decode_grid(const DecodeArgs& a) {
-  const int pad = 8 * (a.xcd_run > 4 ? a.xcd_run : 4);
-  return (a.num_items + pad - 1) / pad * pad;
+  const long long block = 8LL * a.xcd_run;
+  const long long g = ((long long)a.num_items + block - 1) / block * block;
+  return (int)((g + 31) / 32 * 32);
 }
 
 // Orders a wavefront's own LDS writes before its later LDS reads of other lanes' data

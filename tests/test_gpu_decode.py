@@ -261,3 +261,13 @@ def test_kv_head_counts_off_the_xcd_count_match_oracle(G, Hkv):
     cfg = small_cfg(G, 64, "bf16", "bf16", S=5, Hkv=Hkv, ctx=("uniform", 1, 150), max_ctx=150, seed=21)
     _step_case(cfg)
     _step_case(cfg, partition_size=64)
+
+
+@pytest.mark.parametrize("G,Hkv,S", [(4, 3, 24), (2, 3, 24), (4, 3, 40), (4, 6, 24), (3, 5, 30)])
+def test_every_work_item_of_a_short_xcd_run_is_launched(G, Hkv, S):
+    # With 4-sequence workgroups the items run kv head fastest, Hkv per XCD in turn: the grid
+    # must cover whole blocks of 8 * Hkv workgroups (3 kv heads, 6 groups and 3 partitions:
+    # 54 items, which a grid padded to 64 only partly reached).
+    cfg = small_cfg(G, 128, "bf16", "bf16", S=S, Hkv=Hkv, ctx=("uniform", 100, 150), max_ctx=150, seed=23)
+    _step_case(cfg, partition_size=64)
+    _step_case(cfg, partition_size=48)
