@@ -238,8 +238,8 @@ def gpu_bench(args, pool) -> int:
             "workload": cfg.description,
             "num_seqs": cfg.num_seqs, "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
             "head_dim": cfg.head_dim, "block_size": cfg.block_size, "max_context_len": cfg.max_context_len,
-            "partition_tokens": pkv.partition_tokens(cfg.num_seqs, cfg.num_kv_heads, cfg.max_context_len,
-                                                     cfg.partition_size),
+            "partition_tokens": pkv.partition_tokens(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
+                                                     cfg.max_context_len, cfg.partition_size),
             "kv_bytes_algorithmic_per_replica": kv_alg_r, "kv_bytes_logical_per_replica": kv_log_r,
             "copy_pairs": n_pairs,
             "replicas": args.replicas, "seed": cfg.seed, "parallelism": "single GPU",

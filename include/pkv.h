@@ -63,8 +63,9 @@ extern "C" {
 #endif
 
 /* 2: pkv_decode_step and pkv_decode_step_no_alloc take cow_src.
- * 3: pkv_validate_inputs and pkv_validate_inputs_host take cow_src (pkv_validate.h). */
-#define PKV_API_VERSION 3
+ * 3: pkv_validate_inputs and pkv_validate_inputs_host take cow_src (pkv_validate.h).
+ * 4: pkv_decode_partition_tokens takes num_q_heads. */
+#define PKV_API_VERSION 4
 
 /* Element types. */
 typedef enum pkv_dtype {
@@ -92,14 +93,18 @@ const char* pkv_status_string(int status);
 int pkv_api_version(void);
 
 /*
- * Context-partition length, in tokens, that pkv_paged_attention_decode will use.
- * partition_size > 0 is validated and returned as is (it must be a multiple of 16);
- * 0 asks the library to choose: one partition per sequence when num_seqs *
- * num_kv_heads work items already fill the GPU (1024 or more), otherwise the longest
- * multiple of 256 tokens that gives about 1024 items. Returns a negative pkv_status on
- * bad input.
+ * Context-partition length, in tokens, that pkv_paged_attention_decode (and
+ * pkv_decode_step) will use for these sizes. partition_size > 0 is validated and returned
+ * as is (it must be a multiple of 16); 0 asks the library to choose. It aims at 1024
+ * (sequence, kv head, partition) work items for grouped query heads (num_q_heads >
+ * num_kv_heads, the matrix-core kernel) and at 2048 for one query head per kv head (the
+ * vector-ALU kernel): one partition per sequence when num_seqs * num_kv_heads reaches
+ * that, otherwise the shortest multiple of 64 tokens that gives at most about that many
+ * items (the whole context when that is longer). Returns a negative pkv_status on bad
+ * input.
  */
-int pkv_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_context_len, int partition_size);
+int pkv_decode_partition_tokens(int num_seqs, int num_q_heads, int num_kv_heads, int max_context_len,
+                                int partition_size);
 
 /*
  * Bytes of device workspace pkv_paged_attention_decode needs for these sizes (0 when

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 1, 2, 3
 PKV_NO_ALLOC_SCRATCH_BYTES = 32 << 20     # include/pkv.h
-API_VERSION = 3                           # PKV_API_VERSION, include/pkv.h
+API_VERSION = 4                           # PKV_API_VERSION, include/pkv.h
 
 _c_int, _c_i64, _c_f, _c_p, _c_sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -30,7 +30,7 @@ class Validation(ctypes.Structure):
 SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_c_int]),
     "pkv_api_version": (_c_int, []),
-    "pkv_decode_partition_tokens": (_c_int, [_c_int, _c_int, _c_int, _c_int]),
+    "pkv_decode_partition_tokens": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "pkv_paged_attention_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "pkv_paged_attention_decode": (_c_int, [
         _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,            # out q k_cache v_cache block_tables context_lens

@@ -15,10 +15,20 @@ namespace {
 
 constexpr int kMaxGroup = 16;
 constexpr int kMaxPartTokens = 32768;     // block-table slice of one partition: 2048 ids in LDS
-// Work items (sequence, kv head, partition) to aim for when splitting contexts: one per
-// SIMD. Fewer, longer partitions stream longer and leave less to merge; on the 32K-token
-// batch, 2048-token partitions (1024 items) beat 1024-token ones by 3%.
-constexpr int kTargetItems = 1024;
+// Work items (sequence, kv head, partition) to aim for when splitting contexts (measured
+// over partition sizes on small batches):
+// * matrix-core kernel: one per SIMD. Fewer, longer partitions stream longer and leave
+//   less to merge; on the 32K-token batch, 2048-token partitions (1024 items) beat
+//   1024-token ones by 3%, and at 1-2 sequences 128-256-token partitions lose 8-20%;
+// * vector-ALU kernel (one query head per kv head): two per SIMD. Its wavefront keeps
+//   fewer bytes in flight; batches of 4-32 Llama-2-7B-shaped sequences ran 23-34% faster
+//   at 2048 items than at 1024.
+// Partitions are multiples of kPartGrain tokens: short contexts in small batches want
+// short partitions (8 sequences of 512-768 tokens at 8 kv heads: 64-token partitions
+// 13.1 us, 256-token ones 19.6 us).
+constexpr int kTargetItemsMfma = 1024;
+constexpr int kTargetItemsValu = 2048;
+constexpr int kPartGrain = 64;
 constexpr size_t kAlign = 256;
 constexpr size_t kMaxDynamicLds = 65536;  // dynamic LDS a decode workgroup may use
 
@@ -33,16 +43,19 @@ struct Plan {
   size_t ws_bytes;
 };
 
-int resolve_partition(int num_seqs, int num_kv_heads, int max_context_len, int partition_size) {
-  if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return PKV_ERR_SHAPE;
+int resolve_partition(int num_seqs, int num_q_heads, int num_kv_heads, int max_context_len, int partition_size) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      max_context_len < 0)
+    return PKV_ERR_SHAPE;
   if (partition_size < 0 || partition_size % 16 != 0 || partition_size > kMaxPartTokens) return PKV_ERR_SHAPE;
   if (partition_size > 0) return partition_size;
   const int whole = (int)round_up((size_t)(max_context_len > 0 ? max_context_len : 1), 16);
   const long long units = (long long)num_seqs * num_kv_heads;
+  const int target = num_q_heads == num_kv_heads ? kTargetItemsValu : kTargetItemsMfma;
   int part = whole;
-  if (units > 0 && units < kTargetItems) {
-    const long long want = (kTargetItems + units - 1) / units;
-    part = (int)round_up((size_t)((max_context_len + want - 1) / want), 256);
+  if (units > 0 && units < target) {
+    const long long want = (target + units - 1) / units;
+    part = (int)round_up((size_t)((max_context_len + want - 1) / want), kPartGrain);
     if (part > whole) part = whole;
   }
   return part > kMaxPartTokens ? kMaxPartTokens : part;
@@ -50,7 +63,7 @@ int resolve_partition(int num_seqs, int num_kv_heads, int max_context_len, int p
 
 int make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_context_len,
               int partition_size, Plan* plan) {
-  const int part = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+  const int part = resolve_partition(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_size);
   if (part < 0) return part;
   plan->part_tokens = part;
   plan->num_parts = (max_context_len + part - 1) / part;
@@ -118,8 +131,9 @@ const char* pkv_status_string(int status) {
 
 int pkv_api_version(void) { return PKV_API_VERSION; }
 
-int pkv_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_context_len, int partition_size) {
-  return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+int pkv_decode_partition_tokens(int num_seqs, int num_q_heads, int num_kv_heads, int max_context_len,
+                                int partition_size) {
+  return resolve_partition(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_size);
 }
 
 size_t pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

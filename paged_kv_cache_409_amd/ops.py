@@ -73,8 +73,9 @@ def _check(fn: str, status: int) -> None:
         raise PkvError(fn, status)
 
 
-def partition_tokens(num_seqs: int, num_kv_heads: int, max_context_len: int, partition_size: int = 0) -> int:
-    r = _lib.load().pkv_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_size)
+def partition_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_context_len: int,
+                     partition_size: int = 0) -> int:
+    r = _lib.load().pkv_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_size)
     if r < 0:
         raise PkvError("pkv_decode_partition_tokens", r)
     return r

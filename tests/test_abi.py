@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    assert lib.pkv_api_version() == _lib.API_VERSION == 3
+    assert lib.pkv_api_version() == _lib.API_VERSION == 4
     for code in range(0, -8, -1):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(-99) == b"unknown status"
@@ -41,15 +41,20 @@ def test_status_strings_and_version():
 
 def test_partition_choice():
     lib = _lib.load()
+    pt = lib.pkv_decode_partition_tokens      # (num_seqs, num_q_heads, num_kv_heads, max_context_len, size)
     # enough (sequence, kv head) items: one partition per sequence
-    assert lib.pkv_decode_partition_tokens(256, 8, 768, 0) == 768
-    assert lib.pkv_decode_partition_tokens(64, 32, 2048, 0) == 2048
-    # few items: split long contexts
-    assert lib.pkv_decode_partition_tokens(8, 8, 32768, 0) == 2048
-    assert lib.pkv_decode_partition_tokens(64, 8, 4096, 0) == 2048      # 512 items: two partitions each
-    assert lib.pkv_decode_partition_tokens(8, 8, 32768, 512) == 512
-    assert lib.pkv_decode_partition_tokens(4, 2, 37, 0) == 48
-    assert lib.pkv_decode_partition_tokens(8, 8, 100, 24) == -2      # not a multiple of 16
+    assert pt(256, 64, 8, 768, 0) == 768                 # 2048 items, grouped heads (target 1024)
+    assert pt(64, 32, 32, 2048, 0) == 2048               # 2048 items, one head per kv head (target 2048)
+    # few items: split long contexts, in multiples of 64 tokens
+    assert pt(8, 32, 8, 32768, 0) == 2048                # 64 items x 16 partitions
+    assert pt(64, 32, 8, 4096, 0) == 2048                # 512 items: two partitions each
+    assert pt(16, 32, 32, 2048, 0) == 512                # one head per kv head: 512 items x 4 partitions
+    assert pt(8, 64, 8, 768, 0) == 64                    # 64 items x 12 partitions of 64 tokens
+    assert pt(256, 8, 1, 768, 0) == 192                  # 256 items x 4 partitions
+    assert pt(8, 32, 8, 32768, 512) == 512               # the caller's size
+    assert pt(4, 2, 2, 37, 0) == 48                      # shorter than one step of 64: whole
+    assert pt(8, 32, 8, 100, 24) == -2                   # not a multiple of 16
+    assert pt(8, 30, 8, 100, 0) == -2                    # query heads not a multiple of kv heads
     ws = lib.pkv_paged_attention_workspace_size
     assert ws(256, 64, 8, 128, 768, 0) == 0
     # 8 seqs * 32 heads * 64 partitions * (2 + 128) floats, each part 256-byte aligned

@@ -11,7 +11,7 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libpkv.so"))
     with pytest.raises(RuntimeError, match="missing"):
-        pkv.partition_tokens(8, 8, 4096)
+        pkv.partition_tokens(8, 32, 8, 4096)
 
 
 def test_host_tensors_are_refused():
