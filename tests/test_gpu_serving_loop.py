@@ -103,3 +103,83 @@ def test_beam_search_steps_match_the_oracle(kv_dtype, G, width, P, partition):
         np.testing.assert_array_equal(torch_bits(k_cache), hk)
         np.testing.assert_array_equal(torch_bits(v_cache), hv)
     assert copies >= R * (width - 1)
+
+
+@pytest.mark.parametrize("kv_dtype,G,P", [("bf16", 8, 16), ("fp8_e4m3", 4, 32), ("f16", 2, 64)])
+def test_chunked_prefill_then_decode_match_the_oracle(kv_dtype, G, P):
+    # Prompts of 90-330 tokens prefilled in chunks of 40-130 tokens, every sequence's next
+    # chunk in one launch ("vLLM推理引擎PagedAttention原理与性能优化实战", §六), the block
+    # manager taking the slots; then decode steps over the same caches.
+    rng = np.random.default_rng(71 + G + P)
+    S, Hkv, D, NB, steps = 5, 2, 128, 256, 6
+    q_fmt = "f16" if kv_dtype == "f16" else "bf16"
+    q_t = torch.float16 if q_fmt == "f16" else torch.bfloat16
+    fp8 = kv_dtype == "fp8_e4m3"
+    kv_scale = 1 / 64 if fp8 else 1.0
+    scale = D ** -0.5
+    tol = TOL["fp8_e4m3"] if fp8 else TOL[q_fmt]
+    bm = BlockManager(NB, block_size=P)
+    if fp8:
+        k_cache = torch.full((NB, Hkv, P, D), 0x7F, dtype=torch.uint8, device="cuda")
+    else:
+        k_cache = torch.full((NB, Hkv, P, D), float("nan"), dtype=q_t, device="cuda")
+    v_cache = k_cache.clone()
+    hk, hv = torch_bits(k_cache), torch_bits(v_cache)
+
+    def draw(*shape):
+        return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(q_t).cuda()
+
+    prompt = rng.integers(90, 330, size=S)
+    done = np.zeros(S, dtype=np.int64)
+    it = 0
+    while (done < prompt).any():
+        live = [s for s in range(S) if done[s] < prompt[s]]
+        n = np.array([min(int(rng.integers(40, 130)), int(prompt[s] - done[s])) for s in live])
+        slots = []
+        for s, m in zip(live, n):
+            sl = bm.add_sequence(s, int(m))[0] if done[s] == 0 else bm.append(s, int(m))[0]
+            slots.append(sl)
+            done[s] += m
+        slots = np.concatenate(slots)
+        T = int(n.sum())
+        qsl = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        maxb = max(bm.sequence_info(s)[1] for s in live) + 1
+        tables, ctx = bm.block_tables(live, maxb, pad_block=0)
+        q, k, v = draw(T, Hkv * G, D), draw(T, Hkv, D), draw(T, Hkv, D)
+        pkv.reshape_and_cache(k, v, torch.from_numpy(slots).cuda(), k_cache, v_cache, kv_scale, kv_scale)
+        out = torch.empty_like(q)
+        pkv.paged_attention_prefill(out, q, k_cache, v_cache, torch.from_numpy(tables).cuda(),
+                                    torch.from_numpy(ctx).cuda(), torch.from_numpy(qsl).cuda(), scale, int(n.max()),
+                                    kv_scale, kv_scale)
+        hk, hv = cache_ops.reshape_and_cache(torch_bits(k), torch_bits(v), slots, hk, hv, q_fmt, kv_dtype,
+                                             kv_scale, kv_scale)
+        ref = attention.paged_prefill_attention(torch_bits(q), hk, hv, tables, ctx, qsl, scale, q_fmt, kv_dtype,
+                                                kv_scale, kv_scale)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        err = float(np.abs(got - ref).max())
+        say("chunked prefill", kv_dtype, G, P, "chunk round", it, "rows", T, "err", err)
+        assert np.isfinite(got).all() and err <= tol, f"chunk round {it}: max abs error {err}"
+        it += 1
+    assert it >= 2
+    for step in range(steps):
+        ids = list(range(S))
+        slots, cow = bm.append_step(ids)
+        assert (cow < 0).all()
+        maxb = max(bm.sequence_info(s)[1] for s in ids) + 1
+        tables, ctx = bm.block_tables(ids, maxb, pad_block=0)
+        q, k, v = draw(S, Hkv * G, D), draw(S, Hkv, D), draw(S, Hkv, D)
+        out = torch.empty_like(q)
+        pkv.decode_step(out, q, k_cache, v_cache, k, v, torch.from_numpy(slots).cuda(), torch.from_numpy(tables).cuda(),
+                        torch.from_numpy(ctx).cuda(), scale, int(ctx.max()), kv_scale, kv_scale)
+        hk, hv = cache_ops.reshape_and_cache(torch_bits(k), torch_bits(v), slots, hk, hv, q_fmt, kv_dtype,
+                                             kv_scale, kv_scale)
+        ref = attention.paged_decode_attention(torch_bits(q), hk, hv, tables, ctx, scale, q_fmt, kv_dtype,
+                                               kv_scale, kv_scale)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        err = float(np.abs(got - ref).max())
+        say("decode after prefill", kv_dtype, G, P, "step", step, "err", err)
+        assert np.isfinite(got).all() and err <= tol, f"decode step {step}: max abs error {err}"
+    np.testing.assert_array_equal(torch_bits(k_cache), hk)
+    np.testing.assert_array_equal(torch_bits(v_cache), hv)
