@@ -74,12 +74,29 @@ def gpu_step(b, partition_size=None):
     return gpu_decode(b, partition_size)
 
 
+def output_half_step(ref: np.ndarray, dtype: torch.dtype) -> np.ndarray:
+    """Half the spacing of the output dtype (q's) around each exact value: the error that
+    rounding the exact result to that dtype makes on its own. A format with p significant
+    bits has spacing 2^(e - p + 1) in the binade [2^e, 2^(e+1)); below the smallest normal
+    binade the spacing stays that of the smallest one."""
+    p, emin = {torch.bfloat16: (8, -126), torch.float16: (11, -14)}[dtype]
+    a = np.abs(np.asarray(ref, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(np.where(a > 0, e, emin), emin)
+    return np.ldexp(1.0, (e - p).astype(np.int64))
+
+
 def max_err(gpu_out: torch.Tensor, ref: np.ndarray, seqs=None) -> float:
+    """Largest error of a GPU attention output against the oracle's exact (fp64) result,
+    beyond the rounding of that result to the output dtype: max |got - ref| - half a step of
+    the output dtype at ref. The tolerance bounds the arithmetic's error; a value of
+    magnitude 4 or more has bf16 neighbours 2^-5 apart, so its rounding alone can exceed
+    1e-2, whatever computes it."""
     g = gpu_out.float().cpu().numpy().astype(np.float64)
     if seqs is not None:
         g = g[list(seqs)]
     assert np.isfinite(g).all(), "non-finite output"
-    return float(np.abs(g - ref).max())
+    return float((np.abs(g - ref) - output_half_step(ref, gpu_out.dtype)).max())
 
 
 def device_batch(cfg: WorkloadConfig, replica: int = 0):

@@ -31,7 +31,7 @@ def _step_case(cfg, partition_size=0):
     kc, vc = oracle_caches_after_step(h)
     ref = oracle_decode(h, kc, vc)
     err = max_err(out, ref)
-    assert err <= tol(cfg), f"{cfg.name}: max abs error {err}"
+    assert err <= tol(cfg), f"{cfg.name}: error {err} beyond the output's rounding"
     return b, out
 
 

@@ -80,5 +80,5 @@ def test_full_size_fused_step(name):
     h, kc, vc, out = _compare(b, None)
     say(name, "oracle over all", cfg.num_seqs, "sequences")
     err = max_err(out, oracle_decode(h, kc, vc))
-    say(name, "max abs error", err)
+    say(name, "error beyond rounding", err)
     assert err <= tol(cfg)

@@ -27,5 +27,5 @@ def test_full_size_step_matches_oracle(name):
     np.testing.assert_array_equal(torch_bits(b.v_cache), vc)
     say(name, "oracle over all", cfg.num_seqs, "sequences")
     err = max_err(out, oracle_decode(h, kc, vc))
-    say(name, "max abs error", err)
+    say(name, "error beyond rounding", err)
     assert err <= tol(cfg)
