@@ -3,7 +3,9 @@ and copy-on-write sources step by step ("vLLM推理引擎PagedAttention原理与
 §3.1-§3.2), beams are pruned and re-forked, and every step is one fused pkv_decode_step
 with its cow_src. The oracle replays the same copies, new-token writes and attention on host
 copies of the caches; both caches must stay equal bit for bit and every step's attention
-within the dtype's tolerance."""
+within the dtype's tolerance. Also: chunked prefill through the manager followed by decode
+steps, and seeded random serving loops (arrivals with prefix-cache hits, forks, ends,
+shuffled batches) through the fused step."""
 import numpy as np
 import pytest
 import torch
@@ -179,3 +181,99 @@ def test_chunked_prefill_then_decode_match_the_oracle(kv_dtype, G, P):
         assert err <= tol, f"decode step {step}: error {err} beyond the output's rounding"
     np.testing.assert_array_equal(torch_bits(k_cache), hk)
     np.testing.assert_array_equal(torch_bits(v_cache), hv)
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_serving_loops_match_the_oracle(seed):
+    # A seeded serving loop: requests arrive (sharing a system prompt when prefix caching is
+    # on, "vLLM推理引擎PagedAttention原理与性能优化实战", §5.1), fork beams next to their
+    # parents (§3.1-§3.2) and end; every step is one fused decode_step over all live
+    # sequences, in batch order or shuffled, with the manager's copy-on-write sources.
+    rng = np.random.default_rng([9100, seed])
+    q_fmt = str(rng.choice(["bf16", "f16"]))
+    kv_dtype = str(rng.choice([q_fmt, "fp8_e4m3"]))
+    Hkv = int(rng.choice([1, 2, 3, 4]))
+    G = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+    D = int(rng.choice([64, 128]))
+    P = int(rng.choice([16, 32, 64]))
+    partition = int(rng.choice([0, 0, 0, 16, 48, 64, 128]))
+    caching = bool(rng.random() < 0.5)
+    steps = int(rng.integers(15, 35))
+    NB = 1536 // (P // 16)
+    fp8 = kv_dtype == "fp8_e4m3"
+    kv_scale = 1 / 64 if fp8 else 1.0
+    tol = TOL["fp8_e4m3"] if fp8 else TOL[q_fmt]
+    q_t = torch.float16 if q_fmt == "f16" else torch.bfloat16
+    scale = D ** -0.5
+    say("random serving loop", seed, q_fmt, kv_dtype, "Hkv", Hkv, "G", G, "D", D, "P", P, "partition", partition,
+        "caching", caching, "steps", steps)
+    bm = BlockManager(NB, block_size=P, prefix_caching=caching)
+    if fp8:
+        k_cache = torch.full((NB, Hkv, P, D), 0x7F, dtype=torch.uint8, device="cuda")
+    else:
+        k_cache = torch.full((NB, Hkv, P, D), float("nan"), dtype=q_t, device="cuda")
+    v_cache = k_cache.clone()
+    hk, hv = torch_bits(k_cache), torch_bits(v_cache)
+    system = rng.integers(0, 30000, size=int(rng.integers(P, 4 * P))).astype(np.int32)
+
+    def draw(*shape):
+        return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(q_t).cuda()
+
+    live, next_id = [], 0
+
+    def new_request():
+        nonlocal hk, hv, next_id
+        own = rng.integers(0, 30000, size=int(rng.integers(1, 200))).astype(np.int32)
+        toks = np.concatenate([system, own]) if caching else own
+        slots, cached = bm.add_sequence(next_id, len(toks), toks)
+        n = len(toks) - cached                      # a prefix-cache hit's blocks are not written again
+        if n:
+            k, v = draw(n, Hkv, D), draw(n, Hkv, D)
+            pkv.reshape_and_cache(k, v, torch.from_numpy(slots[cached:]).cuda(), k_cache, v_cache, kv_scale, kv_scale)
+            hk, hv = cache_ops.reshape_and_cache(torch_bits(k), torch_bits(v), slots[cached:], hk, hv, q_fmt,
+                                                 kv_dtype, kv_scale, kv_scale)
+        live.append(next_id)
+        next_id += 1
+
+    for _ in range(int(rng.integers(1, 5))):
+        new_request()
+    for step in range(steps):
+        r = rng.random()
+        if r < 0.15:
+            new_request()
+        elif r < 0.45 and len(live) < 24:
+            parent = live[int(rng.integers(len(live)))]
+            for _ in range(int(rng.integers(1, 4))):
+                bm.fork(parent, next_id)
+                live.insert(live.index(parent) + 1, next_id)
+                next_id += 1
+        elif r < 0.6 and len(live) > 1:
+            bm.free(live.pop(int(rng.integers(len(live)))))
+        ids = list(live)
+        if rng.random() < 0.2:
+            rng.shuffle(ids)
+        slots, cow = bm.append_step(ids, rng.integers(0, 30000, size=len(ids)).astype(np.int32))
+        maxb = max(bm.sequence_info(s)[1] for s in ids) + int(rng.integers(0, 3))
+        tables, ctx = bm.block_tables(ids, maxb, pad_block=int(rng.integers(NB)))
+        assert pkv.validate_inputs(NB, torch.from_numpy(tables), torch.from_numpy(ctx), torch.from_numpy(slots),
+                                   block_size=P, decode_step=True, cow_src=torch.from_numpy(cow)) == ("ok", -1, 0)
+        S = len(ids)
+        q, k, v = draw(S, Hkv * G, D), draw(S, Hkv, D), draw(S, Hkv, D)
+        out = torch.empty_like(q)
+        pkv.decode_step(out, q, k_cache, v_cache, k, v, torch.from_numpy(slots).cuda(), torch.from_numpy(tables).cuda(),
+                        torch.from_numpy(ctx).cuda(), scale, int(ctx.max()), kv_scale, kv_scale, partition,
+                        cow_src=torch.from_numpy(cow).cuda())
+        pairs = np.array([(int(cow[i]), int(tables[i, (int(ctx[i]) - 1) // P])) for i in range(S) if cow[i] >= 0],
+                         dtype=np.int64).reshape(-1, 2)
+        if len(pairs):
+            (hk,), (hv,) = cache_ops.copy_blocks([hk], [hv], pairs)
+        hk, hv = cache_ops.reshape_and_cache(torch_bits(k), torch_bits(v), slots, hk, hv, q_fmt, kv_dtype,
+                                             kv_scale, kv_scale)
+        ref = attention.paged_decode_attention(torch_bits(q), hk, hv, tables, ctx, scale, q_fmt, kv_dtype,
+                                               kv_scale, kv_scale)
+        torch.cuda.synchronize()
+        err = max_err(out, ref)
+        assert err <= tol, f"step {step}: error {err} beyond the output's rounding ({S} seqs, {len(pairs)} copies)"
+        np.testing.assert_array_equal(torch_bits(k_cache), hk)
+        np.testing.assert_array_equal(torch_bits(v_cache), hv)
+    bm.close()
