@@ -5,7 +5,7 @@ with its cow_src. The oracle replays the same copies, new-token writes and atten
 copies of the caches; both caches must stay equal bit for bit and every step's attention
 within the dtype's tolerance. Also: chunked prefill through the manager followed by decode
 steps, and seeded random serving loops (arrivals with prefix-cache hits, forks, ends,
-shuffled batches) through the fused step."""
+preemption by swapping to pinned host memory and back, shuffled batches) through the fused step."""
 import numpy as np
 import pytest
 import torch
@@ -187,8 +187,9 @@ def test_chunked_prefill_then_decode_match_the_oracle(kv_dtype, G, P):
 def test_random_serving_loops_match_the_oracle(seed):
     # A seeded serving loop: requests arrive (sharing a system prompt when prefix caching is
     # on, "vLLM推理引擎PagedAttention原理与性能优化实战", §5.1), fork beams next to their
-    # parents (§3.1-§3.2) and end; every step is one fused decode_step over all live
-    # sequences, in batch order or shuffled, with the manager's copy-on-write sources.
+    # parents (§3.1-§3.2), are swapped out and back in, and end; every step is one fused
+    # decode_step over all live sequences, in batch order or shuffled, with the manager's
+    # copy-on-write sources.
     rng = np.random.default_rng([9100, seed])
     q_fmt = str(rng.choice(["bf16", "f16"]))
     kv_dtype = str(rng.choice([q_fmt, "fp8_e4m3"]))
@@ -207,19 +208,23 @@ def test_random_serving_loops_match_the_oracle(seed):
     scale = D ** -0.5
     say("random serving loop", seed, q_fmt, kv_dtype, "Hkv", Hkv, "G", G, "D", D, "P", P, "partition", partition,
         "caching", caching, "steps", steps)
-    bm = BlockManager(NB, block_size=P, prefix_caching=caching)
+    NH = NB // 2
+    bm = BlockManager(NB, num_host_blocks=NH, block_size=P, prefix_caching=caching)
     if fp8:
         k_cache = torch.full((NB, Hkv, P, D), 0x7F, dtype=torch.uint8, device="cuda")
     else:
         k_cache = torch.full((NB, Hkv, P, D), float("nan"), dtype=q_t, device="cuda")
     v_cache = k_cache.clone()
     hk, hv = torch_bits(k_cache), torch_bits(v_cache)
+    k_host = torch.zeros((NH,) + tuple(k_cache.shape[1:]), dtype=k_cache.dtype).pin_memory()
+    v_host = torch.zeros_like(k_host).pin_memory()
+    hkh, hvh = torch_bits(k_host), torch_bits(v_host)
     system = rng.integers(0, 30000, size=int(rng.integers(P, 4 * P))).astype(np.int32)
 
     def draw(*shape):
         return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(q_t).cuda()
 
-    live, next_id = [], 0
+    live, swapped, next_id = [], [], 0
 
     def new_request():
         nonlocal hk, hv, next_id
@@ -249,6 +254,25 @@ def test_random_serving_loops_match_the_oracle(seed):
                 next_id += 1
         elif r < 0.6 and len(live) > 1:
             bm.free(live.pop(int(rng.integers(len(live)))))
+        elif r < 0.7 and len(live) > 1 and bm.num_free()[2] >= 40:
+            # Preemption ("vLLM 是什么：PagedAttention 让大模型推理快 2-4 倍，还能撑起更长思维链",
+            # §五): the sequence's blocks go to the pinned host pool.
+            sid = live.pop(int(rng.integers(len(live))))
+            pairs = bm.swap_out(sid)
+            pkv.swap_blocks([k_cache], [v_cache], [k_host], [v_host], torch.from_numpy(pairs).cuda())
+            (hkh,), (hvh,) = cache_ops.swap_blocks([hk], [hv], [hkh], [hvh], pairs)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(torch_bits(k_host), hkh)
+            np.testing.assert_array_equal(torch_bits(v_host), hvh)
+            swapped.append(sid)
+        elif r < 0.8 and swapped:
+            sid = swapped.pop(int(rng.integers(len(swapped))))
+            pairs = bm.swap_in(sid)
+            pkv.swap_blocks([k_host], [v_host], [k_cache], [v_cache], torch.from_numpy(pairs).cuda())
+            (hk,), (hv,) = cache_ops.swap_blocks([hkh], [hvh], [hk], [hv], pairs)
+            live.append(sid)
+        if not live:
+            new_request()
         ids = list(live)
         if rng.random() < 0.2:
             rng.shuffle(ids)
