@@ -7,6 +7,7 @@ import torch
 
 from tests._gpu import (HostBatch, device_batch, gpu_decode, gpu_step, max_err, oracle_caches_after_step,
                         oracle_decode, say, tol)
+from tests._paged import torch_bits
 from workloads import WorkloadConfig
 
 pytestmark = pytest.mark.gpu
@@ -271,3 +272,22 @@ def test_every_work_item_of_a_short_xcd_run_is_launched(G, Hkv, S):
     cfg = small_cfg(G, 128, "bf16", "bf16", S=S, Hkv=Hkv, ctx=("uniform", 100, 150), max_ctx=150, seed=23)
     _step_case(cfg, partition_size=64)
     _step_case(cfg, partition_size=48)
+
+
+@pytest.mark.parametrize("G,dtype,kv_dtype,S,partition", [(1, "f16", "f16", 6000, 0), (8, "bf16", "bf16", 4096, 0),
+                                                          (4, "bf16", "fp8_e4m3", 5000, 16),
+                                                          (2, "f16", "fp8_e4m3", 3001, 0)])
+def test_batches_of_thousands_of_sequences_match_oracle(G, dtype, kv_dtype, S, partition):
+    # Grids of thousands of workgroups (and, split into 16-token partitions, tens of
+    # thousands of work items plus the reduce); short contexts keep the oracle quick.
+    cfg = small_cfg(G, 128, dtype, kv_dtype, S=S, ctx=("uniform", 1, 64), max_ctx=64, seed=29)
+    b = device_batch(cfg)
+    h = HostBatch(b)
+    say(cfg.name, "S", S, "partition", partition)
+    out = gpu_step(b, partition)
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches_after_step(h)
+    np.testing.assert_array_equal(torch_bits(b.k_cache), kc)
+    np.testing.assert_array_equal(torch_bits(b.v_cache), vc)
+    err = max_err(out, oracle_decode(h, kc, vc))
+    assert err <= tol(cfg), f"{cfg.name}: error {err} beyond the output's rounding"
