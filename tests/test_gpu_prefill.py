@@ -175,3 +175,18 @@ def test_long_contexts_walk_past_the_staged_block_ids(kv_dtype):
     cfg = prefill_cfg(8, 128, "bf16", kv_dtype, S=3, Hkv=1, ctx=("fixed", [20000, 16400, 16385]),
                       chunk=("fixed", 40), max_ctx=20000)
     _case(cfg)
+
+
+@pytest.mark.parametrize("G,dtype,kv_dtype", [(8, "bf16", "bf16"), (4, "f16", "f16"), (8, "bf16", "fp8_e4m3")])
+def test_long_prompts_in_one_chunk(G, dtype, kv_dtype):
+    # Whole prompts of 4096 and 3500 tokens and 3000-token chunks after prefixes of 1000 and
+    # 96 tokens: up to 256 row tiles of one (sequence, kv head), the longest items of any case.
+    cfg = prefill_cfg(G, 128, dtype, kv_dtype, S=4, ctx=("fixed", [4096, 3500, 4000, 3096]), chunk=("fixed", 3000),
+                      max_ctx=4096, seed=17)
+    b, h, _ = _case(cfg)
+    n = np.diff(h.query_start_loc)
+    assert n.tolist() == [3000, 3000, 3000, 3000] and h.context_lens.tolist() == [4096, 3500, 4000, 3096]
+    cfg = prefill_cfg(G, 128, dtype, kv_dtype, S=2, ctx=("fixed", [4096, 3500]), chunk=("fixed", 4096),
+                      max_ctx=4096, seed=19)
+    b, h, _ = _case(cfg)
+    assert np.diff(h.query_start_loc).tolist() == [4096, 3500]
