@@ -185,8 +185,8 @@ def test_chunked_prefill_then_decode_match_the_oracle(kv_dtype, G, P):
 
 @pytest.mark.parametrize("seed", range(48))
 def test_random_serving_loops_match_the_oracle(seed):
-    # A seeded serving loop: requests arrive (sharing a system prompt when prefix caching is
-    # on, "vLLM推理引擎PagedAttention原理与性能优化实战", §5.1), fork beams next to their
+    # A seeded serving loop: requests arrive and are prefilled (sharing a system prompt when
+    # prefix caching is on, "vLLM推理引擎PagedAttention原理与性能优化实战", §5.1), fork beams next to their
     # parents (§3.1-§3.2), are swapped out and back in, and end; every step is one fused
     # decode_step over all live sequences, in batch order or shuffled, with the manager's
     # copy-on-write sources.
@@ -237,6 +237,17 @@ def test_random_serving_loops_match_the_oracle(seed):
             pkv.reshape_and_cache(k, v, torch.from_numpy(slots[cached:]).cuda(), k_cache, v_cache, kv_scale, kv_scale)
             hk, hv = cache_ops.reshape_and_cache(torch_bits(k), torch_bits(v), slots[cached:], hk, hv, q_fmt,
                                                  kv_dtype, kv_scale, kv_scale)
+            # The prefill of the uncached part, attending over the cached prefix too.
+            tables, ctx = bm.block_tables([next_id], bm.sequence_info(next_id)[1] + 1, pad_block=0)
+            qsl = np.array([0, n], dtype=np.int32)
+            q = draw(n, Hkv * G, D)
+            out = torch.empty_like(q)
+            pkv.paged_attention_prefill(out, q, k_cache, v_cache, torch.from_numpy(tables).cuda(),
+                                        torch.from_numpy(ctx).cuda(), torch.from_numpy(qsl).cuda(), scale, n, kv_scale,
+                                        kv_scale)
+            ref = attention.paged_prefill_attention(torch_bits(q), hk, hv, tables, ctx, qsl, scale, q_fmt, kv_dtype,
+                                                    kv_scale, kv_scale)
+            assert max_err(out, ref) <= tol, f"prefill of request {next_id} ({n} of {len(toks)} tokens)"
         live.append(next_id)
         next_id += 1
 
