@@ -56,10 +56,16 @@ def prefill_kernel(kv_dtype: str):
 
 
 def kernel_source_hash(sources=DECODE_SOURCES) -> str:
+    """Hash of a kernel's sources and of the compiler flags they are built with (common and per
+    file; include paths, which differ between machines, left out): counters taken from any
+    other build do not describe this one."""
+    from paged_kv_cache_409_amd.build import COMMON, FILE_FLAGS, ROOT as BUILD_ROOT
     h = hashlib.sha256()
+    h.update(" ".join(f for f in COMMON if not f.startswith(BUILD_ROOT)).encode())
     for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
+        h.update(" ".join(FILE_FLAGS.get(os.path.basename(f), [])).encode())
     return h.hexdigest()[:16]
 
 

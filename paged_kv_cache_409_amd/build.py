@@ -31,8 +31,12 @@ COMMON = [
 
 # Extra flags of single sources. The prefill kernel lets no NaN reach a maximum or an
 # exponent, so it is built with relaxed NaN handling: its score maxima then skip the
-# NaN-quieting of matrix-core results (about a tenth of its vector instructions).
-FILE_FLAGS = {"prefill_mfma.hip": ["-fno-honor-nans"], "prefill_lds.hip": ["-fno-honor-nans"]}
+# NaN-quieting of matrix-core results (about a tenth of its vector instructions). The
+# vector-ALU decode kernel is scheduled for instruction-level parallelism, which
+# measured 1.6% faster on a batch of 64 sequences with 32 heads of one kv head each (the
+# matrix-core kernel keeps the default scheduler, under which its beam batches run faster).
+FILE_FLAGS = {"prefill_mfma.hip": ["-fno-honor-nans"], "prefill_lds.hip": ["-fno-honor-nans"],
+              "decode_valu.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
